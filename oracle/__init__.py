@@ -1,0 +1,25 @@
+"""CPU oracle for the sequence-parallel reduce + add + RMSNorm (+FP8) shard path.
+
+TEST INFRASTRUCTURE ONLY.  The product package never imports this package;
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may.  It shares no code with the HIP implementation.
+"""
+
+from .oracle import (  # noqa: F401
+    ORC_BF16,
+    ORC_E4M3,
+    ORC_F32,
+    QUANT_DYNAMIC_TOKEN,
+    QUANT_NONE,
+    QUANT_STATIC_TENSOR,
+    OracleError,
+    bf16_from_double,
+    bf16_from_double_array,
+    bf16_to_double,
+    build,
+    e4m3_from_double,
+    e4m3_from_double_array,
+    e4m3_to_double,
+    reduce_add_rmsnorm,
+    shard_geometry,
+)

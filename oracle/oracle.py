@@ -1,0 +1,194 @@
+"""ctypes wrapper around the plain C oracle (``sprms_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Inputs are numpy
+arrays: float32 arrays for f32 tensors and uint16 arrays holding raw
+bfloat16 bit patterns for bf16 tensors.  The wrapper only marshals arrays;
+every step of the computation is in the C file.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+ORC_F32, ORC_BF16, ORC_E4M3 = 0, 1, 2
+QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sprms_oracle.c")
+# SPRMS_ORACLE_LIB lets the mutation tests load a deliberately broken copy.
+_LIB = os.environ.get("SPRMS_ORACLE_LIB") or os.path.join(_HERE, "liboracle_sprms.so")
+
+# -ffp-contract=off keeps every double operation as written (no fused
+# multiply-add), so the oracle's arithmetic is exactly what its source says.
+GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
+           "-Wextra", "-fPIC", "-shared", "-o", _LIB, _SRC, "-lm"]
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+class _Problem(C.Structure):
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("tp_rank", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("hidden", C.c_int64),
+        ("num_tokens", C.c_int64),
+        ("partial_dtype", C.c_int32),
+        ("act_dtype", C.c_int32),
+        ("out_dtype", C.c_int32),
+        ("residual_rows", C.c_int64),
+        ("deepstack_rows", C.c_int64),
+    ]
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always; used by the repository build step)."""
+    subprocess.run(GCC_CMD, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = C.CDLL(_LIB)
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+    lib.orc_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
+                                       C.POINTER(i64)]
+    lib.orc_shard_geometry.restype = C.c_int
+    lib.orc_reduce_add_rmsnorm.argtypes = [
+        C.POINTER(_Problem), vp, vp, vp, vp, C.c_float, i32, vp, C.c_float, i64, vp, vp, vp,
+        vp, vp, vp]
+    lib.orc_reduce_add_rmsnorm.restype = C.c_int
+    lib.orc_bf16_from_double.argtypes = [C.c_double]
+    lib.orc_bf16_from_double.restype = C.c_uint16
+    lib.orc_bf16_to_double.argtypes = [C.c_uint16]
+    lib.orc_bf16_to_double.restype = C.c_double
+    lib.orc_e4m3_from_double.argtypes = [C.c_double]
+    lib.orc_e4m3_from_double.restype = C.c_uint8
+    lib.orc_e4m3_to_double.argtypes = [C.c_uint8]
+    lib.orc_e4m3_to_double.restype = C.c_double
+    lib.orc_bf16_from_double_n.argtypes = [vp, i64, vp]
+    lib.orc_bf16_from_double_n.restype = None
+    lib.orc_e4m3_from_double_n.argtypes = [vp, i64, vp]
+    lib.orc_e4m3_from_double_n.restype = None
+    _lib = lib
+    return lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return ORC_F32
+    if a.dtype == np.uint16:
+        return ORC_BF16
+    raise OracleError(f"unsupported array dtype {a.dtype} (float32 or uint16 bf16 bits)")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def shard_geometry(num_tokens: int, num_tokens_pad: int, tp: int, rank: int):
+    """(shard_rows, local_start, valid_rows) for rank's contiguous shard."""
+    lib = _load()
+    s, st, v = C.c_int64(), C.c_int64(), C.c_int64()
+    rc = lib.orc_shard_geometry(num_tokens, num_tokens_pad, tp, rank, C.byref(s), C.byref(st),
+                                C.byref(v))
+    if rc != 0:
+        raise OracleError(f"orc_shard_geometry failed: {rc}")
+    return s.value, st.value, v.value
+
+
+def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack=None, *,
+                       tp_rank, num_tokens, out_dtype=ORC_BF16, static_scale=1.0, rows=None,
+                       want_debug=True):
+    """Run the oracle on host arrays.
+
+    partials [tp, S, H]; residual [S or tp*S, H]; weight/bias [H];
+    deepstack None or [S or tp*S, H].  ``rows`` selects shard rows (default
+    all).  Returns a dict with residual_out, out (uint16 bf16 bits, float32 or
+    uint8 e4m3 codes), out_scale (dynamic mode), z and y (float64, if
+    ``want_debug``), all compact over the selected rows.
+    """
+    lib = _load()
+    partials = np.ascontiguousarray(partials)
+    residual = np.ascontiguousarray(residual)
+    weight = np.ascontiguousarray(weight)
+    bias = None if bias is None else np.ascontiguousarray(bias)
+    deepstack = None if deepstack is None else np.ascontiguousarray(deepstack)
+    tp, S, H = partials.shape
+    act = _dtype_code(residual)
+    for name, a in (("weight", weight), ("bias", bias), ("deepstack", deepstack)):
+        if a is not None and _dtype_code(a) != act:
+            raise OracleError(f"{name} dtype differs from the residual dtype")
+    if quant_mode != QUANT_NONE:
+        out_dtype = ORC_E4M3
+    prob = _Problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
+                    partial_dtype=_dtype_code(partials), act_dtype=act, out_dtype=out_dtype,
+                    residual_rows=residual.shape[0],
+                    deepstack_rows=0 if deepstack is None else deepstack.shape[0])
+    if rows is None:
+        n = S
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.shape[0]
+    res_out = np.zeros((n, H), dtype=residual.dtype)
+    out_np = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_E4M3: np.uint8}[out_dtype]
+    out = np.zeros((n, H), dtype=out_np)
+    scale = np.zeros((n,), dtype=np.float32)
+    z = np.zeros((n, H), dtype=np.float64) if want_debug else None
+    y = np.zeros((n, H), dtype=np.float64) if want_debug else None
+    rc = lib.orc_reduce_add_rmsnorm(C.byref(prob), _ptr(partials), _ptr(residual), _ptr(weight),
+                                    _ptr(bias), float(eps), quant_mode, _ptr(deepstack),
+                                    float(static_scale), n, _ptr(rows_arr), _ptr(res_out),
+                                    _ptr(out), _ptr(scale), _ptr(z), _ptr(y))
+    if rc != 0:
+        raise OracleError(f"orc_reduce_add_rmsnorm failed: {rc}")
+    result = {"residual_out": res_out, "out": out, "z": z, "y": y}
+    if quant_mode == QUANT_DYNAMIC_TOKEN:
+        result["out_scale"] = scale
+    return result
+
+
+def bf16_from_double(x: float) -> int:
+    return int(_load().orc_bf16_from_double(float(x)))
+
+
+def bf16_to_double(bits: int) -> float:
+    return float(_load().orc_bf16_to_double(int(bits)))
+
+
+def e4m3_from_double(x: float) -> int:
+    return int(_load().orc_e4m3_from_double(float(x)))
+
+
+def e4m3_to_double(code: int) -> float:
+    return float(_load().orc_e4m3_to_double(int(code)))
+
+
+def bf16_from_double_array(x) -> np.ndarray:
+    """Element-wise orc_bf16_from_double over a float64 array (uint16 bits)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_bf16_from_double_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def e4m3_from_double_array(x) -> np.ndarray:
+    """Element-wise orc_e4m3_from_double over a float64 array (uint8 codes)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_e4m3_from_double_n(_ptr(x), x.size, _ptr(out))
+    return out

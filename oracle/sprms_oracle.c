@@ -1,0 +1,317 @@
+/*
+ * sprms_oracle.c -- plain, slow, obviously-correct CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the CPU
+ * baseline leg of the benchmark; never by the product path.  It shares no
+ * code with the HIP implementation.  Built with gcc -O2 -ffp-contract=off so
+ * every double operation is the one written here.
+ *
+ * What it computes, for one rank's shard (page tags as in sprms_oracle.h):
+ *   1. the sum over the tp partial outputs, i.e. the reduction half of
+ *      ReduceScatter -- an element-wise sum over ranks, after which each rank
+ *      keeps its own contiguous block of tokens ([LongCat] o_proj K-axis TP;
+ *      [SP/FC] §2.1-2.2);
+ *   2. plus the rank's chunk of the deepstack embeddings when present
+ *      ([SP/FC] §2.3: the deepstack add moves after the ReduceScatter and
+ *      uses chunk [tp_rank]);
+ *   3. plus the rank's chunk of the residual (maybe_chunk_residual,
+ *      [SP/FC] §2.3); the sum is written back as the new residual (the fused
+ *      add+norm op returns it);
+ *   4. RMSNorm of that sum with weight and optional bias ([SP/FC] §2.3 and
+ *      [SPquant] §1-§2: RMSNorm is per token);
+ *   5. optional FP8 e4m3 output with a static per-tensor scale or a
+ *      per-token scale max|y|/qmax ([SPquant] §4, quantisation table);
+ *   6. zero on padding rows; their inputs are never read ([PR18671] §5.2,
+ *      §5.3: padding rows of the shard are cleared).
+ *
+ * Readings where the pages leave a step open (each listed in the design
+ * notes): eps inside the square root, mean over H; bias added after the
+ * gain; deepstack added before the residual; the norm and quantiser use the
+ * unrounded sum, not the stored residual; qmax = 448 (OCP e4m3fn);
+ * an all-zero row in dynamic mode gets scale 0 and zero codes.
+ */
+#include "sprms_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- formats */
+
+/* bfloat16 is the upper half of an IEEE binary32: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 stored fraction bits, i.e. 8 significant bits. */
+double orc_bf16_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Nearest bfloat16 value to x, ties to the even significand.  The spacing of
+ * bfloat16 values in the binade [2^(k-1), 2^k) is 2^(k-8); below the
+ * smallest normal 2^-126 it is the subnormal step 2^-133.  Dividing by a
+ * power of two is exact, and rint() in the default rounding mode rounds to
+ * the nearest integer with ties to even, so r*spacing is the correctly
+ * rounded result (r = 256 simply lands on the next power of two).  A result
+ * of 2^128 or more is an overflow: +-inf. */
+uint16_t orc_bf16_from_double(double x) {
+  if (isnan(x)) return 0x7FC0;
+  double a = fabs(x);
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    double spacing;
+    if (a < ldexp(1.0, -126)) {
+      spacing = ldexp(1.0, -133);
+    } else {
+      int k;
+      (void)frexp(a, &k); /* a = m * 2^k, 0.5 <= m < 1 */
+      spacing = ldexp(1.0, k - 8);
+    }
+    r = rint(a / spacing) * spacing;
+    if (r >= ldexp(1.0, 128)) r = INFINITY;
+  }
+  float f = (float)r; /* exact: r is a bfloat16 value */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint16_t bits = (uint16_t)(u >> 16);
+  if (signbit(x)) bits |= 0x8000;
+  return bits;
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits.  Exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN and
+ * there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448. */
+double orc_e4m3_to_double(uint8_t code) {
+  int s = code >> 7;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double v;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Clamp to [-448, 448], then pick by exhaustive search the finite code whose
+ * value is nearest to |x|; on an exact tie take the code with the even
+ * mantissa (magnitude codes are monotone, so neighbours differ in the last
+ * bit).  The sign bit follows the sign of x, zero included. */
+uint8_t orc_e4m3_from_double(double x) {
+  if (isnan(x)) return 0x7F;
+  double a = fabs(x);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double err = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (signbit(x) ? 0x80 : 0x00));
+}
+
+/* --------------------------------------------------------------- elements */
+
+static size_t elt_size(int32_t dt) {
+  switch (dt) {
+    case ORC_F32: return 4;
+    case ORC_BF16: return 2;
+    case ORC_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+static double load(const void* base, int32_t dt, int64_t idx) {
+  if (dt == ORC_F32) {
+    float f;
+    memcpy(&f, (const char*)base + 4 * idx, 4);
+    return (double)f;
+  }
+  uint16_t b;
+  memcpy(&b, (const char*)base + 2 * idx, 2);
+  return orc_bf16_to_double(b);
+}
+
+/* Round once to the storage type (f32: C's conversion, which rounds to
+ * nearest-even in the default mode; bf16: the definition above). */
+static void store(void* base, int32_t dt, int64_t idx, double v) {
+  if (dt == ORC_F32) {
+    float f = (float)v;
+    memcpy((char*)base + 4 * idx, &f, 4);
+  } else if (dt == ORC_BF16) {
+    uint16_t b = orc_bf16_from_double(v);
+    memcpy((char*)base + 2 * idx, &b, 2);
+  } else {
+    ((uint8_t*)base)[idx] = orc_e4m3_from_double(v);
+  }
+}
+
+/* -------------------------------------------------------------- geometry */
+
+int orc_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp,
+                       int32_t rank, int64_t* shard_rows, int64_t* local_start,
+                       int64_t* valid_rows) {
+  if (!shard_rows || !local_start || !valid_rows) return ORC_ERR_NULL;
+  if (tp < 1 || rank < 0 || rank >= tp) return ORC_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens_pad < 0 || num_tokens > num_tokens_pad) return ORC_ERR_SHAPE;
+  if (num_tokens_pad % tp != 0) return ORC_ERR_SHAPE;
+  int64_t S = num_tokens_pad / tp;
+  int64_t start = (int64_t)rank * S;
+  int64_t v = num_tokens - start;
+  if (v > S) v = S;
+  if (v < 0) v = 0;
+  *shard_rows = S;
+  *local_start = start;
+  *valid_rows = v;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------ validation */
+
+static int validate(const orc_problem* p, const void* partials, const void* residual,
+                    const void* weight, int32_t quant_mode, const void* deepstack,
+                    float static_scale, int64_t n_rows, const int64_t* rows,
+                    const void* residual_out, const void* out, const float* out_scale) {
+  if (!p) return ORC_ERR_NULL;
+  if (p->tp < 1 || p->tp_rank < 0 || p->tp_rank >= p->tp) return ORC_ERR_SHAPE;
+  if (p->shard_rows < 0 || p->hidden < 1 || p->num_tokens < 0) return ORC_ERR_SHAPE;
+  if (p->num_tokens > (int64_t)p->tp * p->shard_rows) return ORC_ERR_SHAPE;
+  int64_t S = p->shard_rows;
+  if (p->residual_rows != S && p->residual_rows != (int64_t)p->tp * S) return ORC_ERR_SHAPE;
+  if (deepstack == NULL) {
+    if (p->deepstack_rows != 0) return ORC_ERR_SHAPE;
+  } else if (p->deepstack_rows != S && p->deepstack_rows != (int64_t)p->tp * S) {
+    return ORC_ERR_SHAPE;
+  }
+  if (p->partial_dtype != ORC_F32 && p->partial_dtype != ORC_BF16) return ORC_ERR_DTYPE;
+  if (p->act_dtype != ORC_F32 && p->act_dtype != ORC_BF16) return ORC_ERR_DTYPE;
+  if (quant_mode == ORC_QUANT_NONE) {
+    if (p->out_dtype != ORC_F32 && p->out_dtype != ORC_BF16) return ORC_ERR_DTYPE;
+  } else if (quant_mode == ORC_QUANT_STATIC_TENSOR || quant_mode == ORC_QUANT_DYNAMIC_TOKEN) {
+    if (p->out_dtype != ORC_E4M3) return ORC_ERR_DTYPE;
+  } else {
+    return ORC_ERR_UNSUPPORTED;
+  }
+  if (quant_mode == ORC_QUANT_STATIC_TENSOR && !(isfinite(static_scale) && static_scale > 0.0f))
+    return ORC_ERR_SHAPE;
+  if (n_rows < 0) return ORC_ERR_SHAPE;
+  if (rows == NULL && n_rows != S) return ORC_ERR_SHAPE;
+  if (n_rows > 0) {
+    if (!partials || !residual || !weight || !residual_out || !out) return ORC_ERR_NULL;
+    if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN && !out_scale) return ORC_ERR_NULL;
+  }
+  if (rows)
+    for (int64_t i = 0; i < n_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= S) return ORC_ERR_SHAPE;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------- the path */
+
+int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
+                           const void* residual, const void* weight,
+                           const void* bias, float eps, int32_t quant_mode,
+                           const void* deepstack, float static_scale,
+                           int64_t n_rows, const int64_t* rows,
+                           void* residual_out, void* out, float* out_scale,
+                           double* z_dbg, double* y_dbg) {
+  int rc = validate(p, partials, residual, weight, quant_mode, deepstack, static_scale,
+                    n_rows, rows, residual_out, out, out_scale);
+  if (rc != ORC_OK) return rc;
+
+  const int64_t S = p->shard_rows;
+  const int64_t H = p->hidden;
+  const int64_t tp = p->tp;
+  const int64_t r = p->tp_rank;
+
+  /* valid rows of this shard ([PR18671] §5.2) */
+  int64_t v = p->num_tokens - r * S;
+  if (v > S) v = S;
+  if (v < 0) v = 0;
+  /* maybe_chunk_residual / chunk(deepstack)[tp_rank] ([SP/FC] §2.3): a tensor
+   * holding every rank's rows contributes its block r; a shard-sized tensor
+   * is used as it is. */
+  const int64_t roff = (p->residual_rows == tp * S && tp > 1) ? r * S : 0;
+  const int64_t doff = (deepstack && p->deepstack_rows == tp * S && tp > 1) ? r * S : 0;
+
+  const size_t oz = elt_size(p->out_dtype);
+  const size_t az = elt_size(p->act_dtype);
+  double* z = (double*)malloc((size_t)H * sizeof(double));
+  double* y = (double*)malloc((size_t)H * sizeof(double));
+  if (!z || !y) {
+    free(z);
+    free(y);
+    return ORC_ERR_NULL;
+  }
+
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const int64_t s = rows ? rows[i] : i;
+    if (s >= v) {
+      /* padding row: every output is zero, no input is read */
+      memset((char*)residual_out + (size_t)(i * H) * az, 0, (size_t)H * az);
+      memset((char*)out + (size_t)(i * H) * oz, 0, (size_t)H * oz);
+      if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN) out_scale[i] = 0.0f;
+      if (z_dbg) memset(z_dbg + i * H, 0, (size_t)H * sizeof(double));
+      if (y_dbg) memset(y_dbg + i * H, 0, (size_t)H * sizeof(double));
+      continue;
+    }
+
+    /* z = ((sum over ranks of the partials) + deepstack) + residual */
+    for (int64_t h = 0; h < H; ++h) {
+      double x = 0.0;
+      for (int64_t q = 0; q < tp; ++q) x += load(partials, p->partial_dtype, (q * S + s) * H + h);
+      if (deepstack) x += load(deepstack, p->act_dtype, (doff + s) * H + h);
+      z[h] = x + load(residual, p->act_dtype, (roff + s) * H + h);
+      store(residual_out, p->act_dtype, i * H + h, z[h]);
+    }
+
+    /* RMSNorm: mean of squares over H, eps inside the square root */
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h) ss += z[h] * z[h];
+    const double rstd = 1.0 / sqrt(ss / (double)H + (double)eps);
+
+    /* y = z * rstd * weight (+ bias) and its absolute maximum */
+    double amax = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      y[h] = z[h] * rstd * load(weight, p->act_dtype, h);
+      if (bias) y[h] += load(bias, p->act_dtype, h);
+      if (fabs(y[h]) > amax) amax = fabs(y[h]);
+    }
+
+    if (quant_mode == ORC_QUANT_NONE) {
+      for (int64_t h = 0; h < H; ++h) store(out, p->out_dtype, i * H + h, y[h]);
+    } else if (quant_mode == ORC_QUANT_STATIC_TENSOR) {
+      /* codes encode y / scale, scale a calibrated per-tensor constant */
+      for (int64_t h = 0; h < H; ++h) store(out, ORC_E4M3, i * H + h, y[h] / (double)static_scale);
+    } else {
+      /* per-token scale = max|y| / qmax, qmax = 448; codes encode y / scale */
+      const float scale = (float)(amax / 448.0);
+      out_scale[i] = scale;
+      for (int64_t h = 0; h < H; ++h)
+        store(out, ORC_E4M3, i * H + h, scale > 0.0f ? y[h] / (double)scale : 0.0);
+    }
+
+    if (z_dbg) memcpy(z_dbg + i * H, z, (size_t)H * sizeof(double));
+    if (y_dbg) memcpy(y_dbg + i * H, y, (size_t)H * sizeof(double));
+  }
+  free(z);
+  free(y);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------ array versions */
+
+void orc_bf16_from_double_n(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_from_double(x[i]);
+}
+
+void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_from_double(x[i]);
+}

@@ -1,0 +1,101 @@
+/*
+ * sprms_oracle.h -- plain CPU oracle for the sequence-parallel
+ * "reduce-scatter reduce -> residual add -> RMSNorm (+FP8)" shard path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library includes, links
+ * or calls this code; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no source, header,
+ * constant or table with the HIP implementation.
+ *
+ * Arithmetic is IEEE double throughout; results are rounded once, at the
+ * end, to the requested storage type.
+ *
+ * Pages cited (full titles and addresses are listed in the design notes):
+ *   [SP/FC]    vllm-ascend SP / FlashComm1 / FlashComm2 guide (ai6s.net)
+ *   [LongCat]  LongCat-Flash inference tuning on Atlas A3 (openrokid.csdn.net)
+ *   [SPquant]  vLLM SP / AsyncTP / quantisation notes (beaiera.top)
+ *   [PR18671]  vllm-ascend PR #18671 walkthrough, GLM DSA-CP (huashanblogllm.xyz)
+ */
+#ifndef SPRMS_ORACLE_H
+#define SPRMS_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage types understood by the oracle */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+
+/* output quantisation modes.  Dynamic per-tensor scaling is absent on
+ * purpose: its scale needs the max over every rank's rows, so it cannot be
+ * computed on one shard ([SPquant] §4, table of per-tensor quantisation
+ * correctness). */
+enum { ORC_QUANT_NONE = 0, ORC_QUANT_STATIC_TENSOR = 1, ORC_QUANT_DYNAMIC_TOKEN = 2 };
+
+enum {
+  ORC_OK = 0,
+  ORC_ERR_NULL = -1,
+  ORC_ERR_SHAPE = -2,
+  ORC_ERR_DTYPE = -3,
+  ORC_ERR_UNSUPPORTED = -5
+};
+
+typedef struct {
+  int32_t tp;             /* number of partial sums (tensor-parallel size), >= 1 */
+  int32_t tp_rank;        /* this shard's rank, 0 <= tp_rank < tp */
+  int64_t shard_rows;     /* S: rows per rank after padding (T_pad / tp) */
+  int64_t hidden;         /* H */
+  int64_t num_tokens;     /* T: valid tokens over all ranks, 0 <= T <= tp*S */
+  int32_t partial_dtype;  /* ORC_F32 | ORC_BF16 */
+  int32_t act_dtype;      /* residual, deepstack, weight, bias, residual_out */
+  int32_t out_dtype;      /* ORC_F32 | ORC_BF16 (no quant), ORC_E4M3 (quant) */
+  int64_t residual_rows;  /* S (shard residual) or tp*S (replicated residual) */
+  int64_t deepstack_rows; /* 0 (absent), S or tp*S */
+} orc_problem;
+
+/* Shard layout of [PR18671] §2 and §5.2: contiguous rank shards of
+ * S = T_pad / tp rows; rank r starts at r*S; its valid rows are
+ * max(0, min(S, T - r*S)).  Returns ORC_ERR_SHAPE when T_pad is not a
+ * positive multiple of tp, T > T_pad, or the rank is out of range. */
+int orc_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp,
+                       int32_t rank, int64_t* shard_rows, int64_t* local_start,
+                       int64_t* valid_rows);
+
+/* The whole shard computation for a list of shard rows.
+ *
+ * partials   [tp][S][H]   partial_dtype  (rank q's partial for this shard)
+ * residual   [residual_rows][H] act_dtype
+ * weight     [H] act_dtype;  bias [H] act_dtype or NULL
+ * deepstack  [deepstack_rows][H] act_dtype or NULL
+ * static_scale   used only by ORC_QUANT_STATIC_TENSOR (must be finite, > 0)
+ * rows       n_rows shard-row indices in [0,S); NULL means 0..S-1 (n_rows = S)
+ * Outputs are compact, one row per requested row, in request order:
+ *   residual_out [n_rows][H] act_dtype
+ *   out          [n_rows][H] out_dtype
+ *   out_scale    [n_rows] (dynamic mode; may be NULL otherwise)
+ *   z_dbg, y_dbg [n_rows][H] doubles, optional: the pre-norm sum and the
+ *                normalised value before output rounding (0 on pad rows).
+ * Returns ORC_OK or a negative ORC_ERR_* code; on error nothing is written. */
+int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
+                           const void* residual, const void* weight,
+                           const void* bias, float eps, int32_t quant_mode,
+                           const void* deepstack, float static_scale,
+                           int64_t n_rows, const int64_t* rows,
+                           void* residual_out, void* out, float* out_scale,
+                           double* z_dbg, double* y_dbg);
+
+/* Format helpers, exported so that the tests can pin them directly. */
+uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
+double orc_bf16_to_double(uint16_t bits);
+uint8_t orc_e4m3_from_double(double x);    /* clamp to +-448, nearest, ties to even */
+double orc_e4m3_to_double(uint8_t code);   /* NaN for the two NaN codes */
+void orc_bf16_from_double_n(const double* x, int64_t n, uint16_t* out);
+void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for the shard path, shared by tests and the benchmark.
+
+This module holds shapes, distributions and random draws only: none of the
+path's arithmetic.  Values come from torch's seeded generator on the device
+that will hold them, drawn as float32 N(mu, sigma) and rounded once to the
+storage dtype (torch's cast, round to nearest even).
+
+Workloads (one rank's shard each; shapes follow the pages' worked examples
+where they give one -- vllm-ascend PR #18671 walkthrough §2: 3500 tokens
+padded to 3504 over TP=16, 219 tokens per rank, hidden 8192):
+
+  C1  tp=2,  64 tokens,          S=32,    H=512,  fp32 in, bias, replicated residual
+  C2  tp=8,  1000 -> 1024 tokens, S=128,   H=4096, bf16, 24 padding rows on rank 7
+  C3  tp=16, 3500 -> 3504 tokens, S=219,   H=8192, bf16, bias, 4 padding rows on rank 15
+  C4  tp=8,  65536 tokens,       S=8192,  H=7168, bf16 in, e4m3 out, static scale
+  C5  tp=4,  131072 tokens,      S=32768, H=5120, bf16 in + deepstack, e4m3 out, per-token scale
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN = 0, 1, 2
+
+BASE_SEED = 20261202
+
+# tensor ids folded into the seed, one stream per tensor
+_TID_PARTIALS, _TID_RESIDUAL, _TID_DEEPSTACK, _TID_WEIGHT, _TID_BIAS = 1, 2, 3, 4, 5
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    description: str
+    tp: int
+    num_tokens: int          # valid tokens T over all ranks
+    num_tokens_pad: int      # T_pad, a multiple of tp
+    hidden: int
+    partial_dtype: torch.dtype
+    act_dtype: torch.dtype
+    quant_mode: int
+    out_dtype: torch.dtype   # bf16 / f32 for no quant, uint8 (e4m3 codes) otherwise
+    residual_replicated: bool  # residual holds every rank's rows ([tp*S, H])
+    deepstack: bool            # deepstack present, full [T_pad, H], chunked by rank
+    bias: bool
+    rank: int                  # rank whose shard is timed
+    partial_sigma: float
+    residual_sigma: float = 1.0
+    deepstack_sigma: float = 0.3
+    weight_mu: float = 1.0
+    weight_sigma: float = 0.1
+    bias_sigma: float = 0.02
+    eps: float = 1e-6
+    seed_index: int = 0
+
+    @property
+    def shard_rows(self) -> int:
+        return self.num_tokens_pad // self.tp
+
+    def valid_rows(self, rank: Optional[int] = None) -> int:
+        r = self.rank if rank is None else rank
+        return max(0, min(self.shard_rows, self.num_tokens - r * self.shard_rows))
+
+    def algorithmic_bytes(self, rank: Optional[int] = None) -> int:
+        """Bytes the method must move for one rank's shard: read the tp partials,
+        the residual and deepstack rows of the valid rows, weight and bias once,
+        the static scale once; write residual_out and out for all S rows and
+        the per-token scales."""
+        S, H, v = self.shard_rows, self.hidden, self.valid_rows(rank)
+        pe = torch.tensor([], dtype=self.partial_dtype).element_size()
+        ae = torch.tensor([], dtype=self.act_dtype).element_size()
+        oe = torch.tensor([], dtype=self.out_dtype).element_size()
+        reads = v * H * (self.tp * pe + ae + (ae if self.deepstack else 0))
+        reads += H * ae * (2 if self.bias else 1)
+        reads += 4 if self.quant_mode == QUANT_STATIC_TENSOR else 0
+        writes = S * H * (ae + oe) + (4 * S if self.quant_mode == QUANT_DYNAMIC_TOKEN else 0)
+        return reads + writes
+
+
+WORKLOADS = {
+    "C1": Workload("C1", "tp=2, 64 tokens (32/rank shard), hidden 512, fp32 partials and residual, "
+                   "bias, bf16 out", tp=2, num_tokens=64, num_tokens_pad=64, hidden=512,
+                   partial_dtype=torch.float32, act_dtype=torch.float32, quant_mode=QUANT_NONE,
+                   out_dtype=torch.bfloat16, residual_replicated=True, deepstack=False, bias=True,
+                   rank=1, partial_sigma=1.0, seed_index=0),
+    "C2": Workload("C2", "dense SP threshold: 1000 tokens padded to 1024, tp=8 (128-token shard), "
+                   "hidden 4096, bf16", tp=8, num_tokens=1000, num_tokens_pad=1024, hidden=4096,
+                   partial_dtype=torch.bfloat16, act_dtype=torch.bfloat16, quant_mode=QUANT_NONE,
+                   out_dtype=torch.bfloat16, residual_replicated=False, deepstack=False, bias=False,
+                   rank=7, partial_sigma=0.5, seed_index=1),
+    "C3": Workload("C3", "GLM-like: 3500 tokens padded to 3504, tp=16 (219-token shard), hidden "
+                   "8192, bf16, bias", tp=16, num_tokens=3500, num_tokens_pad=3504, hidden=8192,
+                   partial_dtype=torch.bfloat16, act_dtype=torch.bfloat16, quant_mode=QUANT_NONE,
+                   out_dtype=torch.bfloat16, residual_replicated=False, deepstack=False, bias=True,
+                   rank=15, partial_sigma=0.5, seed_index=2),
+    "C4": Workload("C4", "FP8 static per-tensor: 65536 tokens, tp=8 (8192-token shard), hidden "
+                   "7168, bf16 in, e4m3 out", tp=8, num_tokens=65536, num_tokens_pad=65536,
+                   hidden=7168, partial_dtype=torch.bfloat16, act_dtype=torch.bfloat16,
+                   quant_mode=QUANT_STATIC_TENSOR, out_dtype=torch.uint8,
+                   residual_replicated=False, deepstack=False, bias=False, rank=7,
+                   partial_sigma=0.5, seed_index=3),
+    "C5": Workload("C5", "VL deepstack + per-token dynamic FP8: 131072 tokens, tp=4 (32768-token "
+                   "shard), hidden 5120, bf16 in, e4m3 out + fp32 row scales", tp=4,
+                   num_tokens=131072, num_tokens_pad=131072, hidden=5120,
+                   partial_dtype=torch.bfloat16, act_dtype=torch.bfloat16,
+                   quant_mode=QUANT_DYNAMIC_TOKEN, out_dtype=torch.uint8,
+                   residual_replicated=False, deepstack=True, bias=False, rank=3,
+                   partial_sigma=0.5, seed_index=4),
+}
+
+
+def _normal(shape, mu, sigma, dtype, device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    if mu != 0.0:
+        t.add_(mu)
+    return t if dtype == torch.float32 else t.to(dtype)
+
+
+def _seed(w: Workload, rank: int, tid: int, base: int) -> int:
+    return ((base + w.seed_index) * 131 + rank) * 17 + tid
+
+
+def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed=BASE_SEED,
+                pad_fill: Optional[float] = None, shard_rows: Optional[int] = None):
+    """Seeded inputs for one rank's shard.
+
+    Returns a dict of tensors: partials [tp, S, H], residual ([tp*S, H] when
+    replicated else [S, H]), weight [H], bias [H] or None, deepstack
+    [tp*S, H] or None.  ``pad_fill`` (e.g. NaN) overwrites every input row
+    that belongs to a padding row of this shard, to show they are not read.
+    ``shard_rows`` overrides S (smaller stand-ins of a workload's shape).
+    """
+    r = w.rank if rank is None else rank
+    S = w.shard_rows if shard_rows is None else shard_rows
+    H, tp = w.hidden, w.tp
+    out = {
+        "partials": _normal((tp, S, H), 0.0, w.partial_sigma, w.partial_dtype, device,
+                            _seed(w, r, _TID_PARTIALS, base_seed)),
+        "residual": _normal(((tp * S) if w.residual_replicated else S, H), 0.0, w.residual_sigma,
+                            w.act_dtype, device, _seed(w, r, _TID_RESIDUAL, base_seed)),
+        "weight": _normal((H,), w.weight_mu, w.weight_sigma, w.act_dtype, device,
+                          _seed(w, r, _TID_WEIGHT, base_seed)),
+        "bias": (_normal((H,), 0.0, w.bias_sigma, w.act_dtype, device,
+                         _seed(w, r, _TID_BIAS, base_seed)) if w.bias else None),
+        "deepstack": (_normal((tp * S, H), 0.0, w.deepstack_sigma, w.act_dtype, device,
+                              _seed(w, r, _TID_DEEPSTACK, base_seed)) if w.deepstack else None),
+    }
+    if pad_fill is not None:
+        T = w.num_tokens if shard_rows is None else min(w.num_tokens, tp * S)
+        v = max(0, min(S, T - r * S))
+        if v < S:
+            out["partials"][:, v:, :] = pad_fill
+            roff = r * S if w.residual_replicated else 0
+            out["residual"][roff + v:roff + S] = pad_fill
+            if out["deepstack"] is not None:
+                out["deepstack"][r * S + v:r * S + S] = pad_fill
+    return out

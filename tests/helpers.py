@@ -1,0 +1,51 @@
+"""Test-only helpers: tensor <-> numpy marshalling for the oracle and the
+comparison rules used by the parity tests."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def to_host(t):
+    """torch tensor -> numpy array the oracle understands (float32, or uint16
+    holding bfloat16 bits, or uint8 codes)."""
+    if t is None:
+        return None
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return t.view(torch.uint8).numpy()
+    raise TypeError(t.dtype)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Float32 values -> bf16 bits via torch's cast (a library RNE)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP e4m3fn decode from the format definition (sign, 4-bit exponent with
+    bias 7, 3-bit mantissa; exponent 0 = subnormal; S.1111.111 = NaN)."""
+    c = codes.astype(np.int64)
+    s = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((e == 0xF) & ((c & 7) == 7), np.nan, v)
+    return s * v
+
+
+def e4m3_step(t: np.ndarray) -> np.ndarray:
+    """Spacing of e4m3 values around |t| (the 'one e4m3 step')."""
+    a = np.minimum(np.abs(t), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (e - 3)

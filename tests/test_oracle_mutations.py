@@ -1,0 +1,56 @@
+"""The pins must catch plausible mistakes in the oracle (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source, builds it
+into a temporary library, and runs the pin suite against it in a fresh
+process: the suite must fail.  The product code is never involved.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sprms_oracle.c")
+
+MUTATIONS = {
+    "drop_deepstack": ("if (deepstack) x += load(deepstack", "if (0) x += load(deepstack"),
+    "drop_last_partial": ("for (int64_t q = 0; q < tp; ++q) x +=",
+                          "for (int64_t q = 0; q < tp - 1; ++q) x +="),
+    "eps_outside_sqrt": ("1.0 / sqrt(ss / (double)H + (double)eps)",
+                         "1.0 / (sqrt(ss / (double)H) + (double)eps)"),
+    "mean_over_h_minus_1": ("sqrt(ss / (double)H + ", "sqrt(ss / (double)(H - 1) + "),
+    "bias_subtracted": ("if (bias) y[h] += load(bias", "if (bias) y[h] -= load(bias"),
+    "residual_chunk_ignored": ("(p->residual_rows == tp * S && tp > 1) ? r * S : 0",
+                               "(p->residual_rows == tp * S && tp > 1) ? 0 : 0"),
+    "deepstack_chunk_off_by_one": ("p->deepstack_rows == tp * S && tp > 1) ? r * S : 0",
+                                   "p->deepstack_rows == tp * S && tp > 1) ? r * S + 1 : 0"),
+    "qmax_240": ("(float)(amax / 448.0)", "(float)(amax / 240.0)"),
+    "e4m3_no_tie_to_even": ("(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(0)"),
+    "bf16_ties_away": ("r = rint(a / spacing) * spacing;", "r = floor(a / spacing + 0.5) * spacing;"),
+    "pad_rows_off_by_one": ("if (s >= v) {", "if (s > v) {"),
+    "residual_not_added": ("z[h] = x + load(residual, p->act_dtype, (roff + s) * H + h);",
+                           "z[h] = x;"),
+    "weight_ignored": ("y[h] = z[h] * rstd * load(weight, p->act_dtype, h);",
+                       "y[h] = z[h] * rstd;"),
+    "static_scale_multiplied": ("y[h] / (double)static_scale)", "y[h] * (double)static_scale)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", str(lib), str(mutated), "-lm"],
+                   check=True)
+    env = dict(os.environ, SPRMS_ORACLE_LIB=str(lib))
+    proc = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, f"pins did not catch mutation {name}:\n{proc.stdout[-2000:]}"

@@ -1,0 +1,427 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test ties the oracle to something other than itself: the pages'
+worked example and stated equivalences, closed forms, a textbook routine
+(torch's rms_norm in float64), library roundings (torch's bf16 and e4m3
+casts), format definitions and brute force.  Page tags:
+  [SP/FC]    vllm-ascend SP / FlashComm1 / FlashComm2 guide (ai6s.net)
+  [SPquant]  vLLM SP / AsyncTP / quantisation notes (beaiera.top)
+  [PR18671]  vllm-ascend PR #18671 walkthrough (huashanblogllm.xyz)
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import bf16_bits_to_f64, e4m3_decode, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NONE, STATIC, DYNAMIC = oracle.QUANT_NONE, oracle.QUANT_STATIC_TENSOR, oracle.QUANT_DYNAMIC_TOKEN
+
+
+def f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- formats
+
+
+def test_e4m3_decode_matches_format_definition():
+    # OCP 8-bit floating point spec, E4M3: bias 7, max normal 448, min normal
+    # 2^-6, min subnormal 2^-9, S.1111.111 is NaN, no infinities.
+    assert oracle.e4m3_to_double(0x38) == 1.0
+    assert oracle.e4m3_to_double(0x7E) == 448.0
+    assert oracle.e4m3_to_double(0xFE) == -448.0
+    assert oracle.e4m3_to_double(0x08) == 2.0 ** -6
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9
+    assert oracle.e4m3_to_double(0x07) == 7 / 8 * 2.0 ** -6
+    assert oracle.e4m3_to_double(0x78) == 256.0
+    assert np.isnan(oracle.e4m3_to_double(0x7F)) and np.isnan(oracle.e4m3_to_double(0xFF))
+    vals = [oracle.e4m3_to_double(c) for c in range(256)]
+    finite = [v for v in vals if not np.isnan(v)]
+    assert len(finite) == 254
+    pos = vals[:0x7F]
+    assert all(a < b for a, b in zip(pos, pos[1:]))  # magnitude codes are monotone
+    # independent decode from the definition, element by element
+    ref = e4m3_decode(np.arange(256))
+    np.testing.assert_array_equal(np.isnan(ref), np.isnan(vals))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ref[ok], np.asarray(vals)[ok])
+
+
+@pytest.mark.parametrize("x,code", [
+    (1.0, 0x38), (448.0, 0x7E), (-448.0, 0xFE), (464.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE),
+    (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (-(2.0 ** -10), 0x80), (3 * 2.0 ** -10, 0x02),
+    (1.0625, 0x38),    # tie between 1.0 (0x38) and 1.125 (0x39): even mantissa
+    (1.1875, 0x3A),    # tie between 1.125 (0x39) and 1.25 (0x3A): even mantissa
+    (1.0625 + 1e-9, 0x39), (0.0, 0x00), (-0.0, 0x80), (float("nan"), 0x7F),
+])
+def test_e4m3_encode_fixed_points(x, code):
+    assert oracle.e4m3_from_double(x) == code
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    # torch's float8_e4m3fn cast is a library round-to-nearest-even for
+    # in-range values; sweep random values, all code values and all midpoints.
+    rng = np.random.default_rng(1)
+    codes = np.arange(0x7F)
+    v = e4m3_decode(codes)
+    mids = (v[:-1] + v[1:]) / 2
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000), rng.normal(0, 0.01, 5000),
+        v, -v, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1000)])
+    x = x.astype(np.float32).astype(np.float64)  # torch casts from float32
+    ours = oracle.e4m3_from_double_array(x)
+    theirs = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, theirs)
+
+
+def test_e4m3_saturates():
+    x = np.array([448.0, 449.0, 480.0, 500.0, 1e30, -449.0, -1e30])
+    np.testing.assert_array_equal(oracle.e4m3_from_double_array(x),
+                                  [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+
+
+def test_bf16_encode_matches_torch_cast_on_float32():
+    rng = np.random.default_rng(2)
+    bits = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    x32 = bits.view(np.float32)
+    x32 = x32[np.isfinite(x32)]
+    ties = ((rng.integers(0, 2 ** 16, 5000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    x32 = np.concatenate([x32, ties, rng.normal(0, 1, 50000).astype(np.float32)])
+    ours = oracle.bf16_from_double_array(x32.astype(np.float64))
+    np.testing.assert_array_equal(ours, f32_to_bf16_bits(x32))
+
+
+def test_bf16_encode_rounds_once_from_double():
+    # 1 + 2^-8 is the midpoint between bf16 1.0 and 1 + 2^-7: tie -> even (1.0).
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8) == 0x3F80
+    # a hair above the midpoint must round up; a float32 detour would lose it
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    # 1 + 3*2^-8 is the midpoint between 1+2^-7 (odd) and 1+2^-6 (even)
+    assert oracle.bf16_from_double(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert oracle.bf16_from_double(-2.5) == 0xC020
+    assert oracle.bf16_from_double(3.0e38 * 1.2) == 0x7F80  # overflow to inf
+    assert oracle.bf16_from_double(2.0 ** -133) == 0x0001   # smallest subnormal
+
+
+# --------------------------------------------------------------- geometry
+
+
+def test_shard_geometry_matches_worked_example():
+    with open(os.path.join(GOLDEN, "shard_geometry.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert oracle.shard_geometry(c["num_tokens"], c["num_tokens_pad"], c["tp"], c["rank"]) == (
+            c["shard_rows"], c["local_start"], c["valid_rows"])
+    c = g["cases"][0]
+    pads = sum(c["num_tokens_pad"] // c["tp"] - oracle.shard_geometry(
+        c["num_tokens"], c["num_tokens_pad"], c["tp"], r)[2] for r in range(c["tp"]))
+    assert pads == g["pad_rows_total"]
+
+
+@pytest.mark.parametrize("args", [(10, 12, 5, 0), (13, 12, 4, 0), (10, 12, 4, 4), (10, 12, 4, -1),
+                                  (10, 12, 0, 0)])
+def test_shard_geometry_rejects_bad_layouts(args):
+    with pytest.raises(oracle.OracleError):
+        oracle.shard_geometry(*args)
+
+
+# ------------------------------------------------------------ closed forms
+
+
+def _run(partials, residual, weight, bias=None, eps=0.0, quant=NONE, deepstack=None, tp_rank=0,
+         num_tokens=None, out_dtype=oracle.ORC_F32, static_scale=1.0, rows=None):
+    tp, S, H = np.asarray(partials).shape
+    return oracle.reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant, deepstack,
+                                     tp_rank=tp_rank,
+                                     num_tokens=tp * S if num_tokens is None else num_tokens,
+                                     out_dtype=out_dtype, static_scale=static_scale, rows=rows)
+
+
+def test_closed_form_rmsnorm_rows():
+    # H = 4, two partials, deepstack and residual, eps = 0 unless stated.
+    w = f32([1.5, 2.0, -1.0, 0.5])
+    b = f32([0.25, -0.5, 0.0, 0.125])
+    P = f32([[[1, 0, 0, 0], [-1, -1, -1, -1]],
+             [[1, 0, 0, 0], [-2, -2, -2, -2]]])          # [tp=2][S=2][H=4]
+    D = f32([[0, 0, 0, 0], [0.5, 0.5, 0.5, 0.5]])
+    R = f32([[0, 0, 0, 0], [-1.5, -1.5, -1.5, -1.5]])
+    r = _run(P, R, w, b, deepstack=D)
+    # row 0: z = (2,0,0,0), mean z^2 = 1, so y = (2w0+b0, b1, b2, b3)
+    # row 1: z = -4 everywhere, mean z^2 = 16, rstd = 1/4, so y = -w + b
+    np.testing.assert_array_equal(r["residual_out"], [[2, 0, 0, 0], [-4, -4, -4, -4]])
+    np.testing.assert_array_equal(r["out"], [[3.25, -0.5, 0.0, 0.125],
+                                            [-1.25, -2.5, 1.0, -0.375]])
+
+
+def test_closed_form_eps_inside_sqrt_and_mean_over_h():
+    # z = (1,1,1,1): mean z^2 = 1; with eps = 3, rstd = 1/sqrt(1+3) = 1/2.
+    # (eps outside the root, or a divisor of H-1, gives a different value.)
+    w = f32([1.0, 2.0, 4.0, -8.0])
+    P = f32([[[1, 1, 1, 1]]])
+    r = _run(P, f32([[0, 0, 0, 0]]), w, eps=3.0)
+    np.testing.assert_array_equal(r["out"], [[0.5, 1.0, 2.0, -4.0]])
+
+
+def test_closed_form_bf16_output_bits():
+    w = f32_to_bf16_bits(np.array([1.5, 2.0, -1.0, 0.5], np.float32))
+    b = f32_to_bf16_bits(np.array([0.25, -0.5, 0.0, 0.125], np.float32))
+    P = f32([[[1, 0, 0, 0]], [[1, 0, 0, 0]]])
+    r = oracle.reduce_add_rmsnorm(P, f32_to_bf16_bits(np.zeros((1, 4), np.float32)), w, b, 0.0,
+                                  NONE, tp_rank=0, num_tokens=1, out_dtype=oracle.ORC_BF16)
+    np.testing.assert_array_equal(r["out"], f32_to_bf16_bits(np.array([[3.25, -0.5, 0, 0.125]],
+                                                                       np.float32)))
+
+
+def test_textbook_rmsnorm_special_case():
+    # tp = 1, no deepstack, zero residual: plain RMSNorm, checked against
+    # torch.nn.functional.rms_norm in float64 (a library routine).
+    rng = np.random.default_rng(3)
+    H = 96
+    z = rng.normal(0, 2, (1, 7, H)).astype(np.float32)
+    w = rng.normal(1, 0.1, H).astype(np.float32)
+    b = rng.normal(0, 0.02, H).astype(np.float32)
+    eps = np.float32(1e-6)
+    r = _run(z, np.zeros((7, H), np.float32), w, b, eps=float(eps))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(z[0]).double(), (H,),
+                                       weight=torch.from_numpy(w).double(), eps=float(eps))
+    ref = ref + torch.from_numpy(b).double()
+    np.testing.assert_allclose(r["y"], ref.numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(r["out"], ref.numpy().astype(np.float32))
+
+
+def test_multi_partial_sum_is_exact_with_integers():
+    # small integers: every partial must be summed exactly once
+    rng = np.random.default_rng(4)
+    tp, S, H = 5, 3, 16
+    P = rng.integers(-8, 9, (tp, S, H)).astype(np.float32)
+    R = rng.integers(-8, 9, (S, H)).astype(np.float32)
+    D = rng.integers(-8, 9, (S, H)).astype(np.float32)
+    r = _run(P, R, np.ones(H, np.float32), deepstack=D)
+    np.testing.assert_array_equal(r["residual_out"], P.sum(0) + D + R)
+
+
+# -------------------------------------------------- the pages' equivalences
+
+
+def _all_ranks_setup(tp=4, T=10, T_pad=12, H=16, seed=5, deepstack=True):
+    rng = np.random.default_rng(seed)
+    full = rng.normal(0, 0.5, (tp, T_pad, H)).astype(np.float32)   # rank q's full partial
+    R = rng.normal(0, 1, (T_pad, H)).astype(np.float32)
+    D = rng.normal(0, 0.3, (T_pad, H)).astype(np.float32) if deepstack else None
+    w = rng.normal(1, 0.1, H).astype(np.float32)
+    b = rng.normal(0, 0.02, H).astype(np.float32)
+    return full, R, D, w, b
+
+
+@pytest.mark.parametrize("quant", [NONE, STATIC, DYNAMIC])
+def test_reduce_scatter_plus_all_gather_equals_all_reduce(quant):
+    # [SP/FC] §2.2: RS followed by AG reproduces AR, and a per-token norm on
+    # each shard equals the norm after gathering.  Path A: one shard holding
+    # every row (the all-reduce path).  Path B: every rank on its own
+    # contiguous slice (replicated residual and full deepstack chunked by
+    # rank), concatenated in rank order and unpadded.
+    tp, T, T_pad, H = 4, 10, 12, 16
+    full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
+    S = T_pad // tp
+    kw = dict(quant=quant, static_scale=0.01, eps=1e-6,
+              out_dtype=oracle.ORC_BF16 if quant == NONE else oracle.ORC_E4M3)
+    A = _run(full, R, w, b, deepstack=D, tp_rank=0, num_tokens=T, **kw)
+    B = [_run(np.ascontiguousarray(full[:, r * S:(r + 1) * S]), R, w, b, deepstack=D, tp_rank=r,
+              num_tokens=T, **kw) for r in range(tp)]
+    for key in ["residual_out", "out", "z", "y"] + (["out_scale"] if quant == DYNAMIC else []):
+        cat = np.concatenate([x[key] for x in B])
+        np.testing.assert_array_equal(cat[:T], A[key][:T], err_msg=key)
+        assert not np.any(cat[T:]), key  # padding rows of the last rank are zero
+
+
+def test_shard_residual_equals_replicated_chunk():
+    # maybe_chunk_residual ([SP/FC] §2.3): a replicated residual contributes
+    # its block [tp_rank]; passing that block directly gives the same result.
+    tp, T, T_pad, H = 4, 12, 12, 8
+    full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
+    S = T_pad // tp
+    for r in range(tp):
+        Pr = np.ascontiguousarray(full[:, r * S:(r + 1) * S])
+        a = _run(Pr, R, w, b, deepstack=D, tp_rank=r, eps=1e-6)
+        c = _run(Pr, np.ascontiguousarray(R[r * S:(r + 1) * S]), w, b,
+                 deepstack=np.ascontiguousarray(D[r * S:(r + 1) * S]), tp_rank=r, eps=1e-6)
+        for key in ("residual_out", "out", "y"):
+            np.testing.assert_array_equal(a[key], c[key])
+
+
+def test_row_selection_matches_full_run():
+    tp, T, T_pad, H = 4, 11, 12, 8
+    full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
+    S = T_pad // tp
+    Pr = np.ascontiguousarray(full[:, 3 * S:])
+    a = _run(Pr, R, w, b, deepstack=D, tp_rank=3, num_tokens=T, eps=1e-6, quant=DYNAMIC)
+    rows = [2, 0, 1]
+    c = _run(Pr, R, w, b, deepstack=D, tp_rank=3, num_tokens=T, eps=1e-6, quant=DYNAMIC,
+             rows=rows)
+    for key in ("residual_out", "out", "out_scale", "y"):
+        np.testing.assert_array_equal(a[key][rows], c[key])
+
+
+# ------------------------------------------------------------- quantisation
+
+
+def test_dynamic_per_token_closed_form():
+    # z = (1,1,1,1): y = w exactly (eps 0).  amax = 1, scale = 1/448 and the
+    # codes encode 448*w: 448 -> 0x7E, -224 -> 0xF6, 112 -> 0x6E, 56 -> 0x66.
+    w = f32([1.0, -0.5, 0.25, 0.125])
+    P = f32([[[1, 1, 1, 1], [0, 0, 0, 0]]])
+    r = _run(P, f32([[0, 0, 0, 0], [0, 0, 0, 0]]), w, quant=DYNAMIC, eps=1e-6,
+             out_dtype=oracle.ORC_E4M3)
+    r0 = _run(P[:, :1], f32([[0, 0, 0, 0]]), w, quant=DYNAMIC, eps=0.0, out_dtype=oracle.ORC_E4M3)
+    np.testing.assert_array_equal(r0["out"][0], [0x7E, 0xF6, 0x6E, 0x66])
+    assert r0["out_scale"][0] == np.float32(1.0 / 448.0)
+    # an all-zero valid row: scale 0 and zero codes
+    assert r["out_scale"][1] == 0.0 and not np.any(r["out"][1])
+
+
+def test_dynamic_per_token_brute_force():
+    # per row: scale = max|y| / 448 found by a linear scan; the argmax
+    # element maps to +-448; every code is the nearest e4m3 value to y/scale.
+    rng = np.random.default_rng(6)
+    tp, S, H = 3, 5, 40
+    P = rng.normal(0, 0.5, (tp, S, H)).astype(np.float32)
+    R = rng.normal(0, 1, (S, H)).astype(np.float32)
+    w = rng.normal(1, 0.1, H).astype(np.float32)
+    r = _run(P, R, w, quant=DYNAMIC, eps=1e-6, out_dtype=oracle.ORC_E4M3)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(P.astype(np.float64).sum(0) + R), (H,),
+                                       weight=torch.from_numpy(w).double(), eps=1e-6).numpy()
+    for s in range(S):
+        amax = max(abs(v) for v in ref[s])
+        assert abs(r["out_scale"][s] - amax / 448) <= 1e-6 * amax / 448
+        t = ref[s] / np.float64(r["out_scale"][s])
+        dec = e4m3_decode(r["out"][s])
+        k = int(np.argmax(np.abs(ref[s])))
+        assert r["out"][s][k] in (0x7E, 0xFE)
+        grid = e4m3_decode(np.arange(0x7F))
+        for j in range(H):  # nearest by exhaustive search over the grid
+            best = grid[np.argmin(np.abs(grid - min(abs(t[j]), 448.0)))]
+            assert abs(dec[j]) == best or abs(abs(dec[j]) - abs(t[j])) == abs(best - abs(t[j]))
+
+
+def test_static_quant_and_saturation():
+    rng = np.random.default_rng(7)
+    tp, S, H = 2, 4, 32
+    P = rng.normal(0, 0.5, (tp, S, H)).astype(np.float32)
+    R = rng.normal(0, 1, (S, H)).astype(np.float32)
+    w = rng.normal(1, 0.1, H).astype(np.float32)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(P.astype(np.float64).sum(0) + R), (H,),
+                                       weight=torch.from_numpy(w).double(), eps=1e-6).numpy()
+    amax = np.abs(ref).max()
+    s = np.float32(amax / 448)
+    r = _run(P, R, w, quant=STATIC, eps=1e-6, static_scale=float(s), out_dtype=oracle.ORC_E4M3)
+    codes = r["out"]
+    k = np.unravel_index(np.argmax(np.abs(ref)), ref.shape)
+    assert codes[k] in (0x7E, 0xFE)
+    np.testing.assert_allclose(e4m3_decode(codes), ref / s, rtol=2.0 ** -4, atol=2.0 ** -10)
+    # half the calibrated scale: everything above 448 saturates to +-448
+    r2 = _run(P, R, w, quant=STATIC, eps=1e-6, static_scale=float(s) / 2, out_dtype=oracle.ORC_E4M3)
+    big = np.abs(ref / (s / 2)) > 448
+    assert big.any()
+    np.testing.assert_array_equal(np.abs(e4m3_decode(r2["out"][big])), 448.0)
+
+
+# ---------------------------------------------------------------- invariants
+
+
+def test_power_of_two_scale_invariance():
+    # eps = 0: scaling every input by 2^k scales z by 2^k exactly and leaves
+    # y, bf16 out, codes and per-token scales unchanged.
+    rng = np.random.default_rng(8)
+    tp, S, H = 4, 3, 24
+    P = rng.normal(0, 0.5, (tp, S, H)).astype(np.float32)
+    R = rng.normal(0, 1, (S, H)).astype(np.float32)
+    D = rng.normal(0, 0.3, (S, H)).astype(np.float32)
+    w = rng.normal(1, 0.1, H).astype(np.float32)
+    for quant in (NONE, DYNAMIC):
+        od = oracle.ORC_BF16 if quant == NONE else oracle.ORC_E4M3
+        a = _run(P, R, w, deepstack=D, quant=quant, out_dtype=od)
+        c = _run(P * 8, R * 8, w, deepstack=D * 8, quant=quant, out_dtype=od)
+        np.testing.assert_array_equal(c["residual_out"], a["residual_out"] * 8)
+        np.testing.assert_array_equal(c["out"], a["out"])
+        np.testing.assert_allclose(c["y"], a["y"], rtol=1e-15)
+
+
+def test_padding_rows_are_zero_and_never_read():
+    # [PR18671] §5.2/§5.3: padding rows of the shard are zeroed.  Fill their
+    # inputs with NaN: outputs on padding rows must be exactly 0, no NaN anywhere.
+    tp, T, T_pad, H = 4, 9, 12, 8
+    full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
+    S = T_pad // tp
+    r = tp - 1
+    v = T - r * S  # 0 valid rows on the last rank
+    Pr = np.ascontiguousarray(full[:, r * S:])
+    Pr[:, v:] = np.nan
+    R2, D2 = R.copy(), D.copy()
+    R2[r * S + v:] = np.nan
+    D2[r * S + v:] = np.nan
+    for quant in (NONE, STATIC, DYNAMIC):
+        out = _run(Pr, R2, w, b, deepstack=D2, tp_rank=r, num_tokens=T, eps=1e-6, quant=quant,
+                   static_scale=0.01, out_dtype=oracle.ORC_BF16 if quant == NONE else oracle.ORC_E4M3)
+        for key, val in out.items():
+            if val is None:
+                continue
+            assert not np.any(np.isnan(val.astype(np.float64))), key
+            assert not np.any(val[v:]), key
+
+
+def test_partial_shard_padding():
+    tp, T, T_pad, H = 4, 10, 12, 8
+    full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
+    S = T_pad // tp
+    Pr = np.ascontiguousarray(full[:, 3 * S:])
+    Pr[:, 1:] = np.nan
+    out = _run(Pr, R, w, b, deepstack=D, tp_rank=3, num_tokens=T, eps=1e-6,
+               out_dtype=oracle.ORC_BF16)
+    assert np.all(np.isfinite(out["y"][0])) and np.any(out["out"][0])
+    assert not np.any(out["out"][1:]) and not np.any(out["residual_out"][1:])
+
+
+# ---------------------------------------------------------------- validation
+
+
+@pytest.mark.parametrize("case", ["rank", "tokens", "residual_rows", "deepstack_rows",
+                                  "quant_dyn_tensor", "static_scale_zero", "static_scale_inf"])
+def test_oracle_rejects_invalid_problems(case):
+    tp, S, H = 2, 3, 8
+    P = np.zeros((tp, S, H), np.float32)
+    R = np.zeros((S, H), np.float32)
+    w = np.ones(H, np.float32)
+    kw = dict(tp_rank=0, num_tokens=tp * S, out_dtype=oracle.ORC_F32)
+    args = [P, R, w, None, 1e-6, NONE, None]
+    if case == "rank":
+        kw["tp_rank"] = 2
+    elif case == "tokens":
+        kw["num_tokens"] = tp * S + 1
+    elif case == "residual_rows":
+        args[1] = np.zeros((S + 1, H), np.float32)
+    elif case == "deepstack_rows":
+        args[6] = np.zeros((S + 2, H), np.float32)
+    elif case == "quant_dyn_tensor":
+        args[5] = 3  # dynamic per-tensor has no shard-local scale
+    elif case == "static_scale_zero":
+        args[5] = STATIC
+        kw["static_scale"] = 0.0
+    elif case == "static_scale_inf":
+        args[5] = STATIC
+        kw["static_scale"] = float("inf")
+    with pytest.raises(oracle.OracleError):
+        oracle.reduce_add_rmsnorm(*args, **kw)
+
+
+def test_bf16_inputs_are_decoded_exactly():
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F], np.uint16)
+    np.testing.assert_array_equal(bf16_bits_to_f64(bits),
+                                  [oracle.bf16_to_double(int(b)) for b in bits])
+    assert oracle.bf16_to_double(0x3F80) == 1.0 and oracle.bf16_to_double(0xC000) == -2.0
