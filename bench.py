@@ -1,0 +1,220 @@
+"""Benchmark of the fused shard path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5]
+
+One step = one call of sp_reduce_add_rmsnorm over the whole shard of the
+workload's timed rank (every stage of the path in one kernel), inputs
+already resident in HBM.  Prints one JSON line: whole-job HBM throughput
+over the algorithmic bytes (GB/s), the roofline of the kernel (per-launch
+HIP-event durations on the launch stream), and the CPU oracle timed on a
+bounded sample of the same shard.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import reduce_add_rmsnorm_amd as sp  # noqa: E402
+from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_STATIC_TENSOR,  # noqa: E402
+                                           WORKLOADS, make_inputs)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) + shard tokens/s for fused reduce-add-RMSNorm"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+KERNEL_SRC = os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc", "sprms.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3"}
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"<!--\s*traffic\s+(\{.*?\})\s*-->", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(workload)
+    if not rec or rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def static_scale() -> float:
+    with open(os.path.join(ROOT, "tests", "golden", "c4_static_scale.json")) as f:
+        return float(json.load(f)["scale"])
+
+
+def setup(w, dev):
+    x = make_inputs(w, rank=w.rank, device=dev)
+    S, H = w.shard_rows, w.hidden
+    out = torch.empty((S, H), dtype=w.out_dtype, device=dev)
+    res_out = torch.empty((S, H), dtype=w.act_dtype, device=dev)
+    scale = None
+    if w.quant_mode == QUANT_STATIC_TENSOR:
+        scale = torch.tensor([static_scale()], dtype=torch.float32, device=dev)
+    elif w.quant_mode == QUANT_DYNAMIC_TOKEN:
+        scale = torch.empty((S,), dtype=torch.float32, device=dev)
+    launch = sp.prepare(x["partials"], x["residual"], x["weight"], x["bias"], w.eps, w.quant_mode,
+                        x["deepstack"], out, scale, tp_rank=w.rank, num_tokens=w.num_tokens,
+                        residual_out=res_out)
+    return x, launch, (out, res_out, scale)
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """The C oracle on the first rows of the same shard, single-threaded."""
+    import oracle  # CPU checker; only this leg of the benchmark uses it
+
+    def bits(t):
+        t = t.contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    S = w.shard_rows
+    r = w.rank
+    roff = r * S if w.residual_replicated else 0
+
+    def sample(n):
+        P = bits(x["partials"][:, :n])
+        R = bits(x["residual"][roff:roff + n])
+        D = None if x["deepstack"] is None else bits(x["deepstack"][r * S:r * S + n])
+        wt = bits(x["weight"])
+        b = None if x["bias"] is None else bits(x["bias"])
+        return P, R, D, wt, b
+
+    def run(n):
+        P, R, D, wt, b = sample(n)
+        t0 = time.perf_counter()
+        oracle.reduce_add_rmsnorm(P, R, wt, b, w.eps, w.quant_mode, D, tp_rank=r,
+                                  num_tokens=w.tp * n,
+                                  out_dtype=oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
+                                  else oracle.ORC_E4M3,
+                                  static_scale=static_scale() if w.quant_mode == QUANT_STATIC_TENSOR
+                                  else 1.0, want_debug=False)
+        return time.perf_counter() - t0
+
+    t_probe = run(8) / 8
+    n = int(min(S, max(8, budget_s / max(t_probe, 1e-9))))
+    secs = run(n)
+    per_row = w.algorithmic_bytes() / S  # all rows valid in the timed workloads
+    return {
+        "value": round(n * per_row / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {n} of {S} rows of the rank-{r} shard ({w.name}); {secs:.1f} s; "
+                  f"{n / secs:.1f} shard tokens/s",
+        "tokens_per_s": round(n / secs, 2),
+        "seconds": round(secs, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fused shard kernel runs on one rank's shard "
+              "and no collective is part of this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp.load()
+    x, launch, _ = setup(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"# {w.name}: {w.description}; rank {w.rank}; S={w.shard_rows} H={w.hidden} "
+          f"tp={w.tp}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1000.0 / args.steps
+    nbytes = w.algorithmic_bytes()
+    value = nbytes / (ms_per_step / 1000.0) / 1e9
+    avg_ms = statistics.fmean(per_launch_ms)
+    achieved = nbytes / (avg_ms / 1000.0) / 1e9
+    traffic = measured_traffic(w.name)
+    v = w.valid_rows()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
+            "shard_rows": w.shard_rows, "hidden": w.hidden,
+            "quant": QUANT_NAMES[w.quant_mode], "deepstack": w.deepstack, "bias": w.bias,
+            "algorithmic_bytes": nbytes,
+        },
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "shard_tokens_per_s": round(v / (ms_per_step / 1000.0), 1),
+        "kernel_us": {
+            "mean": round(avg_ms * 1000, 2),
+            "median": round(statistics.median(per_launch_ms) * 1000, 2),
+            "p10": round(float(np.percentile(per_launch_ms, 10)) * 1000, 2),
+            "p90": round(float(np.percentile(per_launch_ms, 90)) * 1000, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

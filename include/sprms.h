@@ -1,0 +1,152 @@
+/*
+ * sprms.h -- C ABI of libsprms: the fused per-shard hot path that sequence
+ * parallelism puts between ReduceScatter and AllGather, on one MI355X
+ * (gfx950).
+ *
+ * In the tensor-parallel tail "AllReduce -> RMSNorm", sequence parallelism
+ * splits the AllReduce into ReduceScatter + AllGather and runs the per-token
+ * norm (and any per-token quantiser) on each rank's contiguous token shard
+ * in between (vllm-ascend SP / FlashComm1 / FlashComm2 guide, ai6s.net,
+ * §2.1-§2.3; vLLM SP / AsyncTP / quantisation notes, beaiera.top, §1-§4).
+ * For one rank's shard this library computes, in one kernel launch:
+ *
+ *   z[s][h]  = ((sum over q=0..tp-1 of P[q][s][h]) + D[s][h]) + R[s][h]   (fp32, rank order)
+ *   residual_out[s][h] = z[s][h]                                         (rounded to act dtype)
+ *   y[s][h]  = z[s][h] * rsqrt(mean_h z[s][h]^2 + eps) * w[h] (+ b[h])
+ *   out      = y (bf16 / f32), or FP8 e4m3 codes of y / scale with
+ *              scale a static per-tensor constant or max_h |y[s][h]| / 448
+ *   rows s >= valid_rows: residual_out, out and out_scale are 0; their
+ *              inputs are not read.
+ *
+ * The sum over q is the reduction half of ReduceScatter: element-wise sum of
+ * every rank's partial, each rank keeping its own block of tokens
+ * (LongCat-Flash on Atlas A3, openrokid.csdn.net, "o_proj TP K-axis split").
+ * One rank's input is emulated as partials[tp][S][H]: the slice
+ * [r*S, (r+1)*S) of every rank's partial GEMM output.
+ *
+ * All entry points are plain C; pointers named "device" are HIP device
+ * pointers (e.g. torch tensor data_ptr() on a ROCm build), everything else
+ * is host memory.  The library allocates nothing, keeps no state between
+ * calls other than the thread-local last-error text, and never synchronises.
+ */
+#ifndef SPRMS_H
+#define SPRMS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types. */
+typedef enum { SP_F32 = 0, SP_BF16 = 1, SP_FP8_E4M3 = 2 } sp_dtype;
+
+/* Output quantisation.  Static per-tensor and dynamic per-token scales are
+ * computable on one shard; dynamic per-tensor is not (its max spans every
+ * rank's rows), so it is not offered (vLLM SP / AsyncTP / quantisation notes,
+ * §4, per-tensor quantisation correctness table). */
+typedef enum {
+  SP_QUANT_NONE = 0,           /* out = y in out_dtype (SP_BF16 or SP_F32) */
+  SP_QUANT_STATIC_TENSOR = 1,  /* out = e4m3(y / out_scale[0]), out_scale read */
+  SP_QUANT_DYNAMIC_TOKEN = 2   /* out_scale[s] = max_h|y| / 448, out = e4m3(y / out_scale[s]) */
+} sp_quant;
+
+typedef enum {
+  SP_OK = 0,
+  SP_ERR_NULL = -1,        /* a required pointer is NULL */
+  SP_ERR_SHAPE = -2,       /* inconsistent sizes, rank or row counts */
+  SP_ERR_DTYPE = -3,       /* unsupported dtype combination */
+  SP_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+  SP_ERR_UNSUPPORTED = -5, /* unknown quant mode (includes dynamic per-tensor) */
+  SP_ERR_HIP = -6          /* the kernel launch failed */
+} sp_status;
+
+/* Problem descriptor (host memory, read during the call only). */
+typedef struct {
+  int32_t tp;             /* number of partials = tensor-parallel size, 1 <= tp <= 64 */
+  int32_t tp_rank;        /* 0 <= tp_rank < tp */
+  int64_t shard_rows;     /* S = T_pad / tp, 0 <= S <= 2^31 - 1 */
+  int64_t hidden;         /* H, 8 <= H <= 32768, H % 8 == 0 */
+  int64_t num_tokens;     /* valid tokens T over all ranks, 0 <= T <= tp * S */
+  int32_t partial_dtype;  /* SP_F32 | SP_BF16 */
+  int32_t act_dtype;      /* residual, deepstack, weight, bias, residual_out: SP_F32 | SP_BF16 */
+  int32_t out_dtype;      /* SP_BF16 | SP_F32 with SP_QUANT_NONE; SP_FP8_E4M3 with a quant mode */
+  int64_t residual_rows;  /* S (shard residual) or tp*S (replicated: block tp_rank is used) */
+  int64_t deepstack_rows; /* 0 iff deepstack == NULL, else S or tp*S (block tp_rank is used) */
+  void* residual_out;     /* device [S][H] act_dtype, or NULL: write the used residual rows in place */
+} sp_problem;
+
+/*
+ * sp_reduce_add_rmsnorm -- enqueue the fused shard path on `stream`.
+ *
+ * Defined by: the replacement pattern ReduceScatter -> maybe_chunk_residual
+ * -> fused add + RMSNorm (+bias) -> AllGather, and the deepstack variant
+ * that adds chunk [tp_rank] of the deepstack embeddings after the
+ * ReduceScatter (vllm-ascend SP / FlashComm guide, §2.3); the quantiser
+ * moved onto the shard (vLLM SP / AsyncTP / quantisation notes, §4); the
+ * contiguous shard, valid-row rule and zeroed padding rows (vllm-ascend
+ * PR #18671 walkthrough, §2, §5.2, §5.3).
+ *
+ * Arguments (device pointers, 16-byte aligned, row-major, no row padding):
+ *   p          problem descriptor (host)
+ *   partials   [tp][S][H] partial_dtype: partial q's rows of this shard
+ *   residual   [residual_rows][H] act_dtype; written in place when
+ *              p->residual_out == NULL (only the rows of block tp_rank)
+ *   weight     [H] act_dtype
+ *   bias       [H] act_dtype, or NULL (no bias)
+ *   eps        >= 0, added to the mean of squares inside the square root
+ *   quant_mode sp_quant
+ *   deepstack  [deepstack_rows][H] act_dtype, or NULL
+ *   out        [S][H] out_dtype (e4m3 codes are one byte each)
+ *   out_scale  SP_QUANT_STATIC_TENSOR: [1] f32 scale, read on the device (> 0);
+ *              SP_QUANT_DYNAMIC_TOKEN: [S] f32, written; SP_QUANT_NONE: ignored
+ *   stream     hipStream_t to enqueue on (NULL = default stream)
+ *
+ * Arithmetic: fp32 throughout; partial sums in ascending rank order, then
+ * deepstack, then residual; the norm and the quantiser use the unrounded fp32
+ * sum; stores round to nearest even; e4m3 values are clamped to +-448.
+ * A dynamic row whose max |y| is 0 gets scale 0 and zero codes.
+ *
+ * Ownership and errors: the caller owns every buffer; out and residual_out
+ * must not overlap any input (residual_out may be NULL for in-place).  Every
+ * check runs on the host before anything is enqueued, so a call that
+ * returns an error has written nothing.  Returns SP_OK or a negative
+ * sp_status; sp_last_error() gives the detail.  S == 0 enqueues nothing.
+ * Rows outside [0, S) of out / residual_out are never touched.
+ */
+int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
+                          const void* weight, const void* bias, float eps, int quant_mode,
+                          const void* deepstack, void* out, float* out_scale, void* stream);
+
+/*
+ * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.
+ * Same arguments (no stream); touches no device memory and makes no HIP
+ * call.  Returns SP_OK or the status sp_reduce_add_rmsnorm would return
+ * before launching.
+ */
+int sp_validate(const sp_problem* p, const void* partials, const void* residual,
+                const void* weight, const void* bias, float eps, int quant_mode,
+                const void* deepstack, const void* out, const float* out_scale);
+
+/*
+ * sp_shard_geometry -- contiguous shard layout (vllm-ascend PR #18671
+ * walkthrough, §2 and §5.2): S = num_tokens_pad / tp, local_start = rank*S,
+ * valid_rows = max(0, min(S, num_tokens - local_start)).  Host only.
+ * Returns SP_ERR_SHAPE when num_tokens_pad is not a multiple of tp,
+ * num_tokens > num_tokens_pad, a count is negative or rank is out of range;
+ * SP_ERR_NULL for a NULL output pointer.
+ */
+int sp_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp, int32_t rank,
+                      int64_t* shard_rows, int64_t* local_start, int64_t* valid_rows);
+
+/* Static text for a status code (never NULL). */
+const char* sp_error_string(int status);
+
+/* Detail of the last failing call on this thread (static storage, never NULL). */
+const char* sp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPRMS_H */

@@ -1,0 +1,201 @@
+"""Python binding of libsprms: fused sequence-parallel reduce + add + RMSNorm (+FP8)
+for one rank's token shard on MI355X (gfx950).
+
+The functions here have the names of the C entry points in include/sprms.h
+and only marshal arguments: torch tensors are passed as device pointers, the
+stream is torch's current HIP stream.  Every step of the computation runs in
+the HIP kernels of libsprms.so; there is no other implementation behind these
+names, and they raise if the library is not built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+from .inputs import QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsprms.so")
+
+# sp_dtype
+SP_F32, SP_BF16, SP_FP8_E4M3 = 0, 1, 2
+# sp_quant
+SP_QUANT_NONE, SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN = 0, 1, 2
+# sp_status
+SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED, SP_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+
+EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_shard_geometry", "sp_error_string",
+            "sp_last_error")
+
+
+class SprmsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class sp_problem(C.Structure):
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("tp_rank", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("hidden", C.c_int64),
+        ("num_tokens", C.c_int64),
+        ("partial_dtype", C.c_int32),
+        ("act_dtype", C.c_int32),
+        ("out_dtype", C.c_int32),
+        ("residual_rows", C.c_int64),
+        ("deepstack_rows", C.c_int64),
+        ("residual_out", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(build_if_missing: bool = False):
+    """Load libsprms.so (the built HIP library); raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise ImportError(f"{LIB_PATH} is not built: run `python -m reduce_add_rmsnorm_amd.build`")
+        from .build import build_library
+        build_library()
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    lib.sp_reduce_add_rmsnorm.argtypes = [C.POINTER(sp_problem), vp, vp, vp, vp, C.c_float, C.c_int,
+                                          vp, vp, vp, vp]
+    lib.sp_reduce_add_rmsnorm.restype = C.c_int
+    lib.sp_validate.argtypes = [C.POINTER(sp_problem), vp, vp, vp, vp, C.c_float, C.c_int, vp, vp,
+                                vp]
+    lib.sp_validate.restype = C.c_int
+    lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
+                                      C.POINTER(i64)]
+    lib.sp_shard_geometry.restype = C.c_int
+    lib.sp_error_string.argtypes = [C.c_int]
+    lib.sp_error_string.restype = C.c_char_p
+    lib.sp_last_error.argtypes = []
+    lib.sp_last_error.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _sp_dtype(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return SP_F32
+    if dt == torch.bfloat16:
+        return SP_BF16
+    if dt in (torch.uint8, torch.float8_e4m3fn):
+        return SP_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {dt}")
+
+
+def _addr(x) -> Optional[int]:
+    """Device address of a tensor (must be contiguous), an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("tensors passed to libsprms must be contiguous")
+    return x.data_ptr()
+
+
+def _check(status: int):
+    if status != SP_OK:
+        raise SprmsError(status, sp_last_error())
+
+
+def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deepstack=None,
+                 residual_out=None) -> sp_problem:
+    """sp_problem from tensor shapes and dtypes."""
+    tp, S, H = partials.shape
+    return sp_problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
+                      partial_dtype=_sp_dtype(partials.dtype), act_dtype=_sp_dtype(residual.dtype),
+                      out_dtype=_sp_dtype(out.dtype), residual_rows=residual.shape[0],
+                      deepstack_rows=0 if deepstack is None else deepstack.shape[0],
+                      residual_out=_addr(residual_out))
+
+
+def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack, out,
+                          out_scale, *, tp_rank: int, num_tokens: int, residual_out=None,
+                          stream=None) -> None:
+    """Enqueue the fused shard path (see include/sprms.h for the contract).
+
+    partials [tp, S, H] f32/bf16; residual [S or tp*S, H]; weight, bias [H];
+    deepstack None or [S or tp*S, H]; out [S, H] bf16/f32, or uint8 /
+    float8_e4m3fn for quant modes; out_scale None, [1] f32 (static) or [S]
+    f32 (dynamic); residual_out [S, H] or None (in place).  Runs on
+    ``stream`` (a torch stream or raw hipStream_t int; default: torch's
+    current stream on partials' device).
+    """
+    lib = load()
+    if not partials.is_cuda:
+        raise ValueError("partials must be a device tensor")
+    prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
+                        deepstack=deepstack, residual_out=residual_out)
+    with torch.cuda.device(partials.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(partials.device)
+        handle = stream if isinstance(stream, int) else stream.cuda_stream
+        _check(lib.sp_reduce_add_rmsnorm(C.byref(prob), _addr(partials), _addr(residual),
+                                         _addr(weight), _addr(bias), float(eps), int(quant_mode),
+                                         _addr(deepstack), _addr(out), _addr(out_scale), handle))
+
+
+def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, *,
+            tp_rank: int, num_tokens: int, residual_out=None, stream=None):
+    """Marshal the arguments of sp_reduce_add_rmsnorm once and return a
+    no-argument callable that enqueues the call again (for timing loops).
+    The tensors must stay alive and in place while the callable is used."""
+    lib = load()
+    if not partials.is_cuda:
+        raise ValueError("partials must be a device tensor")
+    prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
+                        deepstack=deepstack, residual_out=residual_out)
+    if stream is None:
+        stream = torch.cuda.current_stream(partials.device)
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    args = (C.byref(prob), _addr(partials), _addr(residual), _addr(weight), _addr(bias),
+            float(eps), int(quant_mode), _addr(deepstack), _addr(out), _addr(out_scale), handle)
+    fn = lib.sp_reduce_add_rmsnorm
+
+    def launch():
+        _check(fn(*args))
+
+    launch.problem = prob  # keep the descriptor alive with the callable
+    return launch
+
+
+def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,
+                out, out_scale) -> int:
+    """Host-side checks only (no HIP call).  Pointer arguments may be tensors,
+    int addresses or None.  Returns the sp_status code."""
+    lib = load()
+    return lib.sp_validate(C.byref(problem), _addr(partials), _addr(residual), _addr(weight),
+                           _addr(bias), float(eps), int(quant_mode), _addr(deepstack), _addr(out),
+                           _addr(out_scale))
+
+
+def sp_shard_geometry(num_tokens: int, num_tokens_pad: int, tp: int, rank: int):
+    """(shard_rows, local_start, valid_rows) of rank's contiguous shard."""
+    lib = load()
+    s, st, v = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(lib.sp_shard_geometry(num_tokens, num_tokens_pad, tp, rank, C.byref(s), C.byref(st),
+                                 C.byref(v)))
+    return s.value, st.value, v.value
+
+
+def sp_error_string(status: int) -> str:
+    return load().sp_error_string(int(status)).decode()
+
+
+def sp_last_error() -> str:
+    return load().sp_last_error().decode()

@@ -1,0 +1,675 @@
+// sprms.hip -- libsprms: fused ReduceScatter-reduce + deepstack/residual add +
+// RMSNorm (+bias) + optional FP8 e4m3 quantisation for one rank's token
+// shard, written for MI355X (gfx950, CDNA4).
+//
+// What is computed is stated in include/sprms.h, with the passages of the
+// pages that define it.  This file is the implementation: host-side
+// validation and dispatch behind the C ABI, and one family of kernels.
+//
+// Kernel design (HBM-bandwidth bound: ~1 flop per byte, no dense
+// contraction, so no MFMA):
+//   * one workgroup per shard row; the row is split into 8-element vectors
+//     (16 B of bf16), thread t owns vectors t, t+NT, ..., t+(VPT-1)NT, so
+//     every load and store instruction of a wavefront covers 1 KiB of
+//     contiguous memory;
+//   * every input vector of the row (tp partials, deepstack, residual, gain,
+//     bias) is loaded into registers before the first add, so each thread has
+//     tp*VPT + 2..4 x VPT 16-byte loads in flight; the sum stays in fp32
+//     registers and nothing is re-read from HBM;
+//   * the updated residual is written once, straight after the adds;
+//   * sum of squares (and, for per-token FP8 without bias, max |z*w|) are
+//     reduced with DPP row operations inside the wavefront, then across
+//     wavefronts through LDS with a single barrier; with a bias the per-token
+//     max needs y, so a second LDS step follows;
+//   * output conversion uses gfx950's v_cvt_pk_bf16_f32 / v_cvt_pk_fp8_f32
+//     (OCP e4m3fn), after an explicit clamp to +-448;
+//   * padding rows (s >= valid_rows) only store zeros.
+// Rows are independent and there is no reuse across rows except the gain and
+// bias vectors (a few KiB, served from L2), so the workgroup -> row mapping
+// needs no XCD-aware swizzle.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sprms.h"
+
+namespace {
+
+constexpr int kVec = 8;  // elements per thread-vector
+constexpr int kMaxThreads = 512;  // workgroup size bound (8 wavefronts)
+constexpr int kMaxWaves = kMaxThreads / 64;
+constexpr int kMaxHidden = kMaxThreads * 8 * kVec;  // 32768
+
+enum OutMode { OM_BF16 = 0, OM_F32 = 1, OM_FP8_STATIC = 2, OM_FP8_DYN = 3 };
+
+struct KArgs {
+  const void* partials;   // [tp][S][H]
+  const void* residual;   // this shard's residual rows (block tp_rank already applied)
+  void* residual_out;     // [S][H]; equals residual for in-place
+  const void* weight;     // [H]
+  const void* bias;       // [H] or nullptr
+  const void* deepstack;  // this shard's deepstack rows or nullptr
+  void* out;              // [S][H]
+  float* out_scale;       // static: [1] (read); dynamic: [S] (written)
+  int64_t plane;          // S*H, distance between partials
+  int32_t H;
+  int32_t nvec;           // H / 8
+  int32_t valid;          // rows [0, valid) are real tokens
+  int32_t tp;
+  float eps;
+};
+
+// ------------------------------------------------------------ element I/O
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <int DT>
+struct Vec;
+
+template <>
+struct Vec<SP_BF16> {
+  using raw = uint4;
+  static __device__ __forceinline__ raw load(const void* base, int64_t e) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+  static __device__ __forceinline__ void unpack(const raw& r, float (&f)[kVec]) {
+    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+  }
+  static __device__ __forceinline__ void add(const raw& r, float (&f)[kVec]) {
+    f[0] += bf16_lo(r.x); f[1] += bf16_hi(r.x);
+    f[2] += bf16_lo(r.y); f[3] += bf16_hi(r.y);
+    f[4] += bf16_lo(r.z); f[5] += bf16_hi(r.z);
+    f[6] += bf16_lo(r.w); f[7] += bf16_hi(r.w);
+  }
+  static __device__ __forceinline__ void store(void* base, int64_t e, const float (&f)[kVec]) {
+    uint4 o;
+    o.x = pack_bf16(f[0], f[1]);
+    o.y = pack_bf16(f[2], f[3]);
+    o.z = pack_bf16(f[4], f[5]);
+    o.w = pack_bf16(f[6], f[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = o;
+  }
+  static __device__ __forceinline__ void store_zero(void* base, int64_t e) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = make_uint4(0, 0, 0, 0);
+  }
+};
+
+template <>
+struct Vec<SP_F32> {
+  struct raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ raw load(const void* base, int64_t e) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e);
+    return raw{p[0], p[1]};
+  }
+  static __device__ __forceinline__ void unpack(const raw& r, float (&f)[kVec]) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+    f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
+  static __device__ __forceinline__ void add(const raw& r, float (&f)[kVec]) {
+    f[0] += r.a.x; f[1] += r.a.y; f[2] += r.a.z; f[3] += r.a.w;
+    f[4] += r.b.x; f[5] += r.b.y; f[6] += r.b.z; f[7] += r.b.w;
+  }
+  static __device__ __forceinline__ void store(void* base, int64_t e, const float (&f)[kVec]) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + e);
+    p[0] = make_float4(f[0], f[1], f[2], f[3]);
+    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  static __device__ __forceinline__ void store_zero(void* base, int64_t e) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + e);
+    p[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    p[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+};
+
+// 8 fp32 -> 8 OCP e4m3fn codes (little-endian byte order = element order),
+// clamped to +-448 first so the conversion never sees an out-of-range value.
+__device__ __forceinline__ uint2 pack_e4m3(const float (&t)[kVec]) {
+  float c[kVec];
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) c[k] = fminf(fmaxf(t[k], -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  return make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+}
+
+// ------------------------------------------------------------- reductions
+
+// DPP move within a wavefront (row = 16 lanes); all controls used here read
+// a valid lane, so bound_ctrl / masks never substitute the old value.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;   // row_ror:4
+constexpr int kRowRor8 = 0x128;   // row_ror:8
+
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes, same fixed order in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kRowRor8>(v);  // every lane now holds its 16-lane row total
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+// ----------------------------------------------------------------- kernel
+
+// PT: partial dtype, AT: activation dtype, OM: output mode,
+// TP: number of partials (0 = runtime, loaded in groups of 4),
+// VPT: 8-element vectors per thread.
+template <int PT, int AT, int OM, int TP, int VPT>
+__global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
+  using VP = Vec<PT>;
+  using VA = Vec<AT>;
+  __shared__ float red[3][kMaxWaves];
+
+  const int64_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int nw = nt >> 6;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int64_t row = s * a.H;
+
+  // Lanes past the end of the row (only when NT*VPT*8 > H) load a valid
+  // element of the row and discard it; they store nothing and add 0.
+  int64_t col[VPT];
+  bool live[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int j = tid + i * nt;
+    live[i] = j < a.nvec;
+    col[i] = static_cast<int64_t>(live[i] ? j : a.nvec - 1) * kVec;
+  }
+
+  if (s >= a.valid) {  // padding row: zeros only, no input is read
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if (!live[i]) continue;
+      VA::store_zero(a.residual_out, row + col[i]);
+      if constexpr (OM == OM_BF16) Vec<SP_BF16>::store_zero(a.out, row + col[i]);
+      if constexpr (OM == OM_F32) Vec<SP_F32>::store_zero(a.out, row + col[i]);
+      if constexpr (OM == OM_FP8_STATIC || OM == OM_FP8_DYN)
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.out) + row + col[i]) = make_uint2(0, 0);
+    }
+    if constexpr (OM == OM_FP8_DYN) {
+      if (tid == 0) a.out_scale[s] = 0.0f;
+    }
+    return;
+  }
+
+  const bool has_ds = a.deepstack != nullptr;
+  const bool has_bias = a.bias != nullptr;
+  float z[VPT][kVec];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) z[i][k] = 0.0f;
+
+  typename VA::raw rw[VPT], rb[VPT];
+  if constexpr (TP > 0) {
+    // ---- every load of the row in flight before the first add
+    typename VP::raw rp[TP][VPT];
+    typename VA::raw rd[VPT], rr[VPT];
+#pragma unroll
+    for (int q = 0; q < TP; ++q)
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) rp[q][i] = VP::load(a.partials, q * a.plane + row + col[i]);
+    if (has_ds) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) rd[i] = VA::load(a.deepstack, row + col[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) rr[i] = VA::load(a.residual, row + col[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) rw[i] = VA::load(a.weight, col[i]);
+    if (has_bias) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) rb[i] = VA::load(a.bias, col[i]);
+    }
+    // sum of partials in ascending rank order, then deepstack, then residual
+#pragma unroll
+    for (int q = 0; q < TP; ++q)
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) VP::add(rp[q][i], z[i]);
+    if (has_ds) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) VA::add(rd[i], z[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) VA::add(rr[i], z[i]);
+  } else {
+    // ---- runtime tp (or too many loads for registers): G partials in
+    // flight at a time, ascending rank order; the rest loaded at use
+    constexpr int kRegsP = PT == SP_F32 ? 8 : 4;
+    constexpr int G = (64 / (VPT * kRegsP)) >= 4 ? 4 : (64 / (VPT * kRegsP)) >= 2 ? 2 : 1;
+    for (int q0 = 0; q0 < a.tp; q0 += G) {
+      typename VP::raw rp[G][VPT];
+      const int g = a.tp - q0 < G ? a.tp - q0 : G;
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+        if (k < g) {
+#pragma unroll
+          for (int i = 0; i < VPT; ++i)
+            rp[k][i] = VP::load(a.partials, (q0 + k) * a.plane + row + col[i]);
+        }
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+        if (k < g) {
+#pragma unroll
+          for (int i = 0; i < VPT; ++i) VP::add(rp[k][i], z[i]);
+        }
+    }
+    if (has_ds) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) VA::add(VA::load(a.deepstack, row + col[i]), z[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) VA::add(VA::load(a.residual, row + col[i]), z[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) rw[i] = VA::load(a.weight, col[i]);
+    if (has_bias) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) rb[i] = VA::load(a.bias, col[i]);
+    }
+  }
+
+  // ---- store the updated residual once
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    if (live[i]) VA::store(a.residual_out, row + col[i], z[i]);
+
+  // ---- zw = z * w; per-thread sum of z^2 and max |zw|
+  float ss = 0.0f, amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    float w[kVec];
+    VA::unpack(rw[i], w);
+    float part = 0.0f, m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      part += z[i][k] * z[i][k];
+      z[i][k] *= w[k];
+      m = fmaxf(m, fabsf(z[i][k]));
+    }
+    if (live[i]) {
+      ss += part;
+      amax = fmaxf(amax, m);
+    }
+  }
+
+  // ---- block reduction: DPP inside the wavefront, LDS across wavefronts
+  constexpr bool kFusedMax = (OM == OM_FP8_DYN);
+  ss = wave_sum(ss);
+  if constexpr (kFusedMax) amax = wave_max(amax);
+  if (lane == 0) {
+    red[0][wave] = ss;
+    if constexpr (kFusedMax) red[1][wave] = amax;
+  }
+  __syncthreads();
+  ss = 0.0f;
+  amax = 0.0f;
+  for (int w = 0; w < nw; ++w) {
+    ss += red[0][w];
+    if constexpr (kFusedMax) amax = fmaxf(amax, red[1][w]);
+  }
+  const float rstd = 1.0f / sqrtf(ss / static_cast<float>(a.H) + a.eps);
+
+  // ---- y = zw * rstd (+ b)
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) z[i][k] *= rstd;
+    if (has_bias) VA::add(rb[i], z[i]);
+  }
+
+  if constexpr (OM == OM_BF16 || OM == OM_F32) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (live[i]) Vec<OM == OM_BF16 ? SP_BF16 : SP_F32>::store(a.out, row + col[i], z[i]);
+    return;
+  } else {
+    float inv;
+    if constexpr (OM == OM_FP8_STATIC) {
+      inv = 1.0f / a.out_scale[0];
+    } else {
+      // max |y|: without bias, rounding is monotone so max|zw*rstd| equals
+      // max|zw| * rstd exactly; with bias it needs a pass over y.
+      float ymax;
+      if (!has_bias) {
+        ymax = amax * rstd;
+      } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+          if (live[i]) {
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) m = fmaxf(m, fabsf(z[i][k]));
+          }
+        m = wave_max(m);
+        if (lane == 0) red[2][wave] = m;
+        __syncthreads();
+        ymax = 0.0f;
+        for (int w = 0; w < nw; ++w) ymax = fmaxf(ymax, red[2][w]);
+      }
+      const float scale = ymax / 448.0f;
+      if (tid == 0) a.out_scale[s] = scale;
+      inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      float t[kVec];
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) t[k] = z[i][k] * inv;
+      if (live[i])
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.out) + row + col[i]) = pack_e4m3(t);
+    }
+  }
+}
+
+// --------------------------------------------------------------- dispatch
+
+using KFn = void (*)(KArgs);
+
+// A compile-time partial count (every load in flight at once) is used while
+// the row's loads fit in about 112 VGPRs; otherwise the grouped path.
+template <int PT, int AT, int TP, int VPT>
+constexpr int fixed_tp() {
+  constexpr int rp = PT == SP_F32 ? 8 : 4, ra = AT == SP_F32 ? 8 : 4;
+  return (TP * VPT * rp + 4 * VPT * ra <= 112) ? TP : 0;
+}
+
+template <int PT, int AT, int OM, int TP>
+KFn pick_vpt(int vpt) {
+  switch (vpt) {
+    case 1: return &sprms_kernel<PT, AT, OM, fixed_tp<PT, AT, TP, 1>(), 1>;
+    case 2: return &sprms_kernel<PT, AT, OM, fixed_tp<PT, AT, TP, 2>(), 2>;
+    case 4: return &sprms_kernel<PT, AT, OM, fixed_tp<PT, AT, TP, 4>(), 4>;
+    case 8: return &sprms_kernel<PT, AT, OM, fixed_tp<PT, AT, TP, 8>(), 8>;
+  }
+  return nullptr;
+}
+
+template <int PT, int AT, int OM>
+KFn pick_tp(int tp, int vpt) {
+  switch (tp) {
+    case 2: return pick_vpt<PT, AT, OM, 2>(vpt);
+    case 4: return pick_vpt<PT, AT, OM, 4>(vpt);
+    case 8: return pick_vpt<PT, AT, OM, 8>(vpt);
+    case 16: return pick_vpt<PT, AT, OM, 16>(vpt);
+    default: return pick_vpt<PT, AT, OM, 0>(vpt);
+  }
+}
+
+template <int PT, int AT>
+KFn pick_om(int om, int tp, int vpt) {
+  switch (om) {
+    case OM_BF16: return pick_tp<PT, AT, OM_BF16>(tp, vpt);
+    case OM_F32: return pick_tp<PT, AT, OM_F32>(tp, vpt);
+    case OM_FP8_STATIC: return pick_tp<PT, AT, OM_FP8_STATIC>(tp, vpt);
+    case OM_FP8_DYN: return pick_tp<PT, AT, OM_FP8_DYN>(tp, vpt);
+  }
+  return nullptr;
+}
+
+KFn pick_kernel(int pt, int at, int om, int tp, int vpt) {
+  if (pt == SP_BF16 && at == SP_BF16) return pick_om<SP_BF16, SP_BF16>(om, tp, vpt);
+  if (pt == SP_F32 && at == SP_F32) return pick_om<SP_F32, SP_F32>(om, tp, vpt);
+  if (pt == SP_BF16 && at == SP_F32) return pick_om<SP_BF16, SP_F32>(om, tp, vpt);
+  if (pt == SP_F32 && at == SP_BF16) return pick_om<SP_F32, SP_BF16>(om, tp, vpt);
+  return nullptr;
+}
+
+// Threads per row: the fewest 8-element vectors per thread (1, 2, 4, 8) that
+// keep the workgroup at <= 512 threads, rounded up to whole wavefronts.
+void launch_shape(int nvec, int* vpt, int* nt) {
+  int v = 1;
+  while (v < 8 && (nvec + v - 1) / v > kMaxThreads) v *= 2;
+  int n = (nvec + v - 1) / v;
+  n = (n + 63) / 64 * 64;
+  *vpt = v;
+  *nt = n;
+}
+
+// ------------------------------------------------------------ host checks
+
+thread_local char g_last_error[512] = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t elt_size(int dt) { return dt == SP_F32 ? 4 : dt == SP_BF16 ? 2 : dt == SP_FP8_E4M3 ? 1 : 0; }
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+struct Plan {
+  int64_t valid;
+  int64_t roff;  // first residual row used
+  int64_t doff;  // first deepstack row used
+};
+
+int check(const sp_problem* p, const void* partials, const void* residual, const void* weight,
+          const void* bias, float eps, int quant_mode, const void* deepstack, const void* out,
+          const float* out_scale, Plan* plan) {
+  if (!p) return fail(SP_ERR_NULL, "problem descriptor is NULL");
+  if (p->tp < 1 || p->tp > 64) return fail(SP_ERR_SHAPE, "tp=%d outside [1, 64]", p->tp);
+  if (p->tp_rank < 0 || p->tp_rank >= p->tp)
+    return fail(SP_ERR_SHAPE, "tp_rank=%d outside [0, tp=%d)", p->tp_rank, p->tp);
+  const int64_t S = p->shard_rows, H = p->hidden, tp = p->tp;
+  if (S < 0 || S > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld outside [0, 2^31)", (long long)S);
+  if (H < 8 || H > kMaxHidden || H % 8 != 0)
+    return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, %d]", (long long)H, kMaxHidden);
+  if (p->num_tokens < 0 || p->num_tokens > tp * S)
+    return fail(SP_ERR_SHAPE, "num_tokens=%lld outside [0, tp*S=%lld]", (long long)p->num_tokens,
+                (long long)(tp * S));
+  if (p->residual_rows != S && p->residual_rows != tp * S)
+    return fail(SP_ERR_SHAPE, "residual_rows=%lld is neither S=%lld nor tp*S=%lld",
+                (long long)p->residual_rows, (long long)S, (long long)(tp * S));
+  if (deepstack == nullptr && p->deepstack_rows != 0)
+    return fail(SP_ERR_SHAPE, "deepstack is NULL but deepstack_rows=%lld", (long long)p->deepstack_rows);
+  if (deepstack != nullptr && p->deepstack_rows != S && p->deepstack_rows != tp * S)
+    return fail(SP_ERR_SHAPE, "deepstack_rows=%lld is neither S=%lld nor tp*S=%lld",
+                (long long)p->deepstack_rows, (long long)S, (long long)(tp * S));
+  if (p->partial_dtype != SP_F32 && p->partial_dtype != SP_BF16)
+    return fail(SP_ERR_DTYPE, "partial_dtype=%d must be SP_F32 or SP_BF16", p->partial_dtype);
+  if (p->act_dtype != SP_F32 && p->act_dtype != SP_BF16)
+    return fail(SP_ERR_DTYPE, "act_dtype=%d must be SP_F32 or SP_BF16", p->act_dtype);
+  if (quant_mode == SP_QUANT_NONE) {
+    if (p->out_dtype != SP_BF16 && p->out_dtype != SP_F32)
+      return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_BF16 or SP_F32 without quantisation", p->out_dtype);
+  } else if (quant_mode == SP_QUANT_STATIC_TENSOR || quant_mode == SP_QUANT_DYNAMIC_TOKEN) {
+    if (p->out_dtype != SP_FP8_E4M3)
+      return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_FP8_E4M3 with quant_mode=%d", p->out_dtype, quant_mode);
+  } else {
+    return fail(SP_ERR_UNSUPPORTED,
+                "quant_mode=%d unsupported (dynamic per-tensor scaling is not shard-local)", quant_mode);
+  }
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SP_ERR_SHAPE, "eps must be finite and >= 0");
+  if (S > 0) {
+    if (!partials || !residual || !weight || !out)
+      return fail(SP_ERR_NULL, "partials, residual, weight and out must be non-NULL");
+    if (quant_mode != SP_QUANT_NONE && !out_scale)
+      return fail(SP_ERR_NULL, "out_scale must be non-NULL with quant_mode=%d", quant_mode);
+  }
+  const void* dev[] = {partials, residual, weight, bias, deepstack, out, p->residual_out};
+  for (const void* d : dev)
+    if (d && misaligned(d)) return fail(SP_ERR_ALIGN, "device pointer %p is not 16-byte aligned", d);
+  if (out_scale && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
+    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", (const void*)out_scale);
+
+  const int64_t r = p->tp_rank;
+  int64_t v = p->num_tokens - r * S;
+  v = v < 0 ? 0 : (v > S ? S : v);
+  plan->valid = v;
+  plan->roff = (p->residual_rows == tp * S) ? r * S : 0;
+  plan->doff = (deepstack && p->deepstack_rows == tp * S) ? r * S : 0;
+
+  // outputs must not overlap inputs (in-place residual excepted)
+  const size_t pe = elt_size(p->partial_dtype), ae = elt_size(p->act_dtype),
+               oe = elt_size(p->out_dtype);
+  const size_t row_a = static_cast<size_t>(H) * ae;
+  const char* res_used = static_cast<const char*>(residual) + plan->roff * row_a;
+  struct Span {
+    const void* p;
+    size_t n;
+  };
+  const Span ins[] = {
+      {partials, static_cast<size_t>(tp * S * H) * pe},
+      {weight, row_a},
+      {bias, bias ? row_a : 0},
+      {deepstack, deepstack ? static_cast<size_t>(p->deepstack_rows) * row_a : 0},
+      {residual, static_cast<size_t>(p->residual_rows) * row_a},
+  };
+  const size_t out_n = static_cast<size_t>(S * H) * oe;
+  for (const Span& in : ins)
+    if (overlap(out, out_n, in.p, in.n)) return fail(SP_ERR_SHAPE, "out overlaps an input");
+  if (p->residual_out && p->residual_out != res_used) {
+    const size_t ro_n = static_cast<size_t>(S) * row_a;
+    for (const Span& in : ins)
+      if (overlap(p->residual_out, ro_n, in.p, in.n))
+        return fail(SP_ERR_SHAPE, "residual_out overlaps an input (pass NULL for in-place)");
+    if (overlap(p->residual_out, ro_n, out, out_n)) return fail(SP_ERR_SHAPE, "residual_out overlaps out");
+  }
+  if (quant_mode == SP_QUANT_DYNAMIC_TOKEN && out_scale) {
+    const size_t sn = static_cast<size_t>(S) * 4;
+    for (const Span& in : ins)
+      if (overlap(out_scale, sn, in.p, in.n)) return fail(SP_ERR_SHAPE, "out_scale overlaps an input");
+    if (overlap(out_scale, sn, out, out_n)) return fail(SP_ERR_SHAPE, "out_scale overlaps out");
+  }
+  return SP_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+int sp_validate(const sp_problem* p, const void* partials, const void* residual, const void* weight,
+                const void* bias, float eps, int quant_mode, const void* deepstack, const void* out,
+                const float* out_scale) {
+  Plan plan;
+  return check(p, partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, &plan);
+}
+
+int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
+                          const void* weight, const void* bias, float eps, int quant_mode,
+                          const void* deepstack, void* out, float* out_scale, void* stream) {
+  Plan plan;
+  int rc = check(p, partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, &plan);
+  if (rc != SP_OK) return rc;
+  if (p->shard_rows == 0) return SP_OK;
+
+  const int64_t H = p->hidden;
+  const size_t ae = elt_size(p->act_dtype);
+  KArgs ka;
+  ka.partials = partials;
+  ka.residual = static_cast<const char*>(residual) + plan.roff * H * ae;
+  ka.residual_out = p->residual_out ? p->residual_out : static_cast<char*>(residual) + plan.roff * H * ae;
+  ka.weight = weight;
+  ka.bias = bias;
+  ka.deepstack = deepstack ? static_cast<const char*>(deepstack) + plan.doff * H * ae : nullptr;
+  ka.out = out;
+  ka.out_scale = out_scale;
+  ka.plane = p->shard_rows * H;
+  ka.H = static_cast<int32_t>(H);
+  ka.nvec = static_cast<int32_t>(H / kVec);
+  ka.valid = static_cast<int32_t>(plan.valid);
+  ka.tp = p->tp;
+  ka.eps = eps;
+
+  const int om = quant_mode == SP_QUANT_STATIC_TENSOR   ? OM_FP8_STATIC
+                 : quant_mode == SP_QUANT_DYNAMIC_TOKEN ? OM_FP8_DYN
+                 : p->out_dtype == SP_BF16              ? OM_BF16
+                                                        : OM_F32;
+  int vpt, nt;
+  launch_shape(ka.nvec, &vpt, &nt);
+  KFn fn = pick_kernel(p->partial_dtype, p->act_dtype, om, p->tp, vpt);
+  if (!fn) return fail(SP_ERR_UNSUPPORTED, "no kernel for this dtype / mode combination");
+  void* args[] = {&ka};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(p->shard_rows)),
+                                 dim3(static_cast<unsigned>(nt)), args, 0,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SP_OK;
+}
+
+int sp_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp, int32_t rank,
+                      int64_t* shard_rows, int64_t* local_start, int64_t* valid_rows) {
+  if (!shard_rows || !local_start || !valid_rows) return fail(SP_ERR_NULL, "output pointer is NULL");
+  if (tp < 1 || rank < 0 || rank >= tp) return fail(SP_ERR_SHAPE, "rank=%d outside [0, tp=%d)", rank, tp);
+  if (num_tokens < 0 || num_tokens_pad < 0 || num_tokens > num_tokens_pad)
+    return fail(SP_ERR_SHAPE, "need 0 <= num_tokens <= num_tokens_pad");
+  if (num_tokens_pad % tp != 0) return fail(SP_ERR_SHAPE, "num_tokens_pad is not a multiple of tp");
+  const int64_t S = num_tokens_pad / tp;
+  const int64_t start = static_cast<int64_t>(rank) * S;
+  int64_t v = num_tokens - start;
+  v = v < 0 ? 0 : (v > S ? S : v);
+  *shard_rows = S;
+  *local_start = start;
+  *valid_rows = v;
+  return SP_OK;
+}
+
+const char* sp_error_string(int status) {
+  switch (status) {
+    case SP_OK: return "success";
+    case SP_ERR_NULL: return "a required pointer is NULL";
+    case SP_ERR_SHAPE: return "inconsistent sizes, rank or row counts";
+    case SP_ERR_DTYPE: return "unsupported dtype combination";
+    case SP_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case SP_ERR_UNSUPPORTED: return "unsupported quantisation mode";
+    case SP_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* sp_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -128,14 +128,16 @@ def _seed(w: Workload, rank: int, tid: int, base: int) -> int:
 
 
 def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed=BASE_SEED,
-                pad_fill: Optional[float] = None, shard_rows: Optional[int] = None):
+                pad_fill: Optional[float] = None, shard_rows: Optional[int] = None,
+                num_tokens: Optional[int] = None):
     """Seeded inputs for one rank's shard.
 
     Returns a dict of tensors: partials [tp, S, H], residual ([tp*S, H] when
     replicated else [S, H]), weight [H], bias [H] or None, deepstack
     [tp*S, H] or None.  ``pad_fill`` (e.g. NaN) overwrites every input row
     that belongs to a padding row of this shard, to show they are not read.
-    ``shard_rows`` overrides S (smaller stand-ins of a workload's shape).
+    ``shard_rows`` and ``num_tokens`` override S and T (smaller stand-ins of
+    a workload's shape; T defaults to min(T, tp*S)).
     """
     r = w.rank if rank is None else rank
     S = w.shard_rows if shard_rows is None else shard_rows
@@ -145,15 +147,16 @@ def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed
                             _seed(w, r, _TID_PARTIALS, base_seed)),
         "residual": _normal(((tp * S) if w.residual_replicated else S, H), 0.0, w.residual_sigma,
                             w.act_dtype, device, _seed(w, r, _TID_RESIDUAL, base_seed)),
+        # gain and bias are replicated on every rank: their seed has no rank
         "weight": _normal((H,), w.weight_mu, w.weight_sigma, w.act_dtype, device,
-                          _seed(w, r, _TID_WEIGHT, base_seed)),
+                          _seed(w, 0, _TID_WEIGHT, base_seed)),
         "bias": (_normal((H,), 0.0, w.bias_sigma, w.act_dtype, device,
-                         _seed(w, r, _TID_BIAS, base_seed)) if w.bias else None),
+                         _seed(w, 0, _TID_BIAS, base_seed)) if w.bias else None),
         "deepstack": (_normal((tp * S, H), 0.0, w.deepstack_sigma, w.act_dtype, device,
                               _seed(w, r, _TID_DEEPSTACK, base_seed)) if w.deepstack else None),
     }
     if pad_fill is not None:
-        T = w.num_tokens if shard_rows is None else min(w.num_tokens, tp * S)
+        T = min(w.num_tokens, tp * S) if num_tokens is None else num_tokens
         v = max(0, min(S, T - r * S))
         if v < S:
             out["partials"][:, v:, :] = pad_fill

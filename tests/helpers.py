@@ -49,3 +49,42 @@ def e4m3_step(t: np.ndarray) -> np.ndarray:
     a = np.minimum(np.abs(t), 448.0)
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
     return 2.0 ** (e - 3)
+
+
+# ----------------------------------------------------------- parity rules
+#
+# The HIP path computes in fp32, the oracle in fp64.  The bars below bound
+# the fp32 rounding of each stage and accept exactly the values that correct
+# rounding of the oracle's value, perturbed within that bound, can give:
+#   z (pre-norm sum): |z32 - z| <= (tp + 3) * 2^-24 * A, A = sum of |terms|
+#   y (normalised):   |y32 - y| <= 2^-17 * (|y - b| + |b|) + err_z * rstd * |w|
+# (2^-17 covers the fp32 sum of squares over H <= 32768 terms, the square
+# root, division and the two products with margin), and then one rounding to
+# the output format.  On top of this the looser published bars (bf16 within
+# 1e-3 + 2^-7 |y|; per-token scales within 1e-5 relative) are asserted.
+
+import oracle  # noqa: E402
+
+U24 = 2.0 ** -24
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f64(oracle.bf16_from_double_array(x))
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    return e4m3_decode(oracle.e4m3_from_double_array(x))
+
+
+def within_rounding(got: np.ndarray, lo: np.ndarray, hi: np.ndarray, rnd) -> np.ndarray:
+    """True where got lies between rnd(lo) and rnd(hi) (rounding is monotone)."""
+    return (got >= rnd(lo)) & (got <= rnd(hi))
+
+
+def z_error(A: np.ndarray, tp: int) -> np.ndarray:
+    return (tp + 3) * U24 * A
+
+
+def y_error(y, b, err_z, rstd, w):
+    b = 0.0 if b is None else b
+    return 2.0 ** -17 * (np.abs(y - b) + np.abs(b)) + err_z * rstd[:, None] * np.abs(w)[None, :]

@@ -1,0 +1,211 @@
+"""GPU-vs-oracle parity driver shared by the GPU tests and the smoke check.
+
+Runs libsprms on seeded inputs (through the C ABI via the binding), runs the
+CPU oracle on the same inputs (copied to the host before the call), and
+checks every computed row with the rules in helpers.py.  Output buffers are
+allocated with a canary row on each side that must come back untouched.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import reduce_add_rmsnorm_amd as sp
+from helpers import (bf16_bits_to_f64, bf16_round, e4m3_decode, e4m3_round, to_host,
+                     within_rounding, y_error, z_error)
+from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR,
+                                           Workload, make_inputs)
+
+CANARY = 0xA5
+
+
+@dataclasses.dataclass
+class Result:
+    rows: np.ndarray
+    valid: int
+    stats: dict
+
+
+def _host_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def _canary_buffer(S: int, H: int, dtype, dev):
+    buf = torch.empty(((S + 2) * H,), dtype=torch.uint8 if dtype == torch.uint8 else dtype,
+                      device=dev)
+    buf.view(torch.uint8).fill_(CANARY)
+    return buf.view(S + 2, H), buf.view(S + 2, H)[1:S + 1]
+
+
+def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optional[int] = None,
+             rows: Optional[Sequence[int]] = None, pad_fill: Optional[float] = float("nan"),
+             in_place: bool = False, out_dtype: Optional[torch.dtype] = None,
+             static_scale: Optional[float] = None, shard_deepstack: bool = False,
+             inputs: Optional[dict] = None, base_seed: Optional[int] = None,
+             require_exact_frac: float = 0.99) -> Result:
+    S = w.shard_rows if S is None else S
+    T = min(w.num_tokens, w.tp * S) if T is None else T
+    kw = {} if base_seed is None else {"base_seed": base_seed}
+    x = inputs if inputs is not None else make_inputs(w, rank=rank, device=dev, shard_rows=S,
+                                                       num_tokens=T, pad_fill=pad_fill, **kw)
+    tp, S_, H = x["partials"].shape
+    assert S_ == S
+    if shard_deepstack and x["deepstack"] is not None and x["deepstack"].shape[0] != S:
+        x["deepstack"] = x["deepstack"][rank * S:(rank + 1) * S].contiguous()
+    quant = w.quant_mode
+    out_dtype = out_dtype or w.out_dtype
+    v = max(0, min(S, T - rank * S))
+
+    # host copies of every input before the call (the residual may be updated in place)
+    h = {k: to_host(t) for k, t in x.items()}
+
+    out_buf, out = _canary_buffer(S, H, out_dtype, dev)
+    res_buf = res_out = None
+    if not in_place:
+        res_buf, res_out = _canary_buffer(S, H, w.act_dtype, dev)
+    scale_t = None
+    if quant == QUANT_STATIC_TENSOR:
+        assert static_scale is not None
+        scale_t = torch.tensor([static_scale], dtype=torch.float32, device=dev)
+    elif quant == QUANT_DYNAMIC_TOKEN:
+        scale_buf = torch.full((S + 2,), float("nan"), dtype=torch.float32, device=dev)
+        scale_t = scale_buf[1:S + 1]
+
+    sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], w.eps,
+                             quant, x["deepstack"], out, scale_t, tp_rank=rank, num_tokens=T,
+                             residual_out=res_out)
+    torch.cuda.synchronize()
+
+    # ---- canaries and untouched memory (byte-exact)
+    ob = out_buf.view(torch.uint8).cpu().numpy().reshape(S + 2, -1)
+    assert (ob[0] == CANARY).all() and (ob[-1] == CANARY).all(), "out canary overwritten"
+    roff = rank * S if x["residual"].shape[0] == tp * S and tp > 1 else 0
+    if res_buf is not None:
+        rb = res_buf.view(torch.uint8).cpu().numpy().reshape(S + 2, -1)
+        assert (rb[0] == CANARY).all() and (rb[-1] == CANARY).all(), "residual_out canary"
+        got_res_full = to_host(res_out)
+        # the input residual is read only
+        np.testing.assert_array_equal(to_host(x["residual"]).view(np.uint8),
+                                      h["residual"].view(np.uint8))
+    else:
+        res_now = to_host(x["residual"])
+        got_res_full = res_now[roff:roff + S]
+        # rows of other ranks' blocks are untouched
+        mask = np.ones(res_now.shape[0], bool)
+        mask[roff:roff + S] = False
+        np.testing.assert_array_equal(res_now[mask].view(np.uint8), h["residual"][mask].view(np.uint8))
+    if quant == QUANT_DYNAMIC_TOKEN:
+        sb = scale_buf.cpu().numpy()
+        assert np.isnan(sb[0]) and np.isnan(sb[-1]), "out_scale canary"
+    for k in ("partials", "weight", "bias", "deepstack"):
+        if x[k] is not None:
+            np.testing.assert_array_equal(to_host(x[k]).view(np.uint8), h[k].view(np.uint8))
+
+    # ---- oracle on the selected rows
+    if rows is None:
+        rows = np.arange(S)
+    rows = np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    ref = oracle.reduce_add_rmsnorm(
+        h["partials"], h["residual"], h["weight"], h["bias"], w.eps, quant, h["deepstack"],
+        tp_rank=rank, num_tokens=T,
+        out_dtype={torch.bfloat16: oracle.ORC_BF16, torch.float32: oracle.ORC_F32}.get(
+            out_dtype, oracle.ORC_E4M3),
+        static_scale=static_scale if static_scale is not None else 1.0, rows=rows)
+
+    stats = {"rows": len(rows), "elements": len(rows) * H}
+    valid = rows < v
+    pad = ~valid
+    got_res = got_res_full[rows]
+    got_out = to_host(out)[rows]
+
+    # ---- padding rows: every output byte zero
+    if pad.any():
+        assert not got_res[pad].view(np.uint8).any(), "residual_out not zero on padding rows"
+        assert not got_out[pad].view(np.uint8).any(), "out not zero on padding rows"
+        if quant == QUANT_DYNAMIC_TOKEN:
+            assert not scale_t.cpu().numpy()[rows[pad]].any(), "out_scale not zero on padding rows"
+    if not valid.any():
+        return Result(rows, v, stats)
+
+    vr = rows[valid]
+    z = ref["z"][valid]
+    y = ref["y"][valid]
+    P = _host_f64(h["partials"][:, vr, :])
+    A = np.abs(P).sum(0) + np.abs(_host_f64(h["residual"][roff + vr]))
+    if h["deepstack"] is not None:
+        doff = rank * S if h["deepstack"].shape[0] == tp * S and tp > 1 else 0
+        A += np.abs(_host_f64(h["deepstack"][doff + vr]))
+    wv = _host_f64(h["weight"])
+    bv = None if h["bias"] is None else _host_f64(h["bias"])
+    err_z = z_error(A, tp)
+    rstd = 1.0 / np.sqrt((z * z).mean(1) + np.float64(np.float32(w.eps)))
+    err_y = y_error(y, bv, err_z, rstd, wv)
+
+    # ---- updated residual
+    gr = _host_f64(got_res[valid])
+    if w.act_dtype == torch.bfloat16:
+        ok = within_rounding(gr, z - err_z, z + err_z, bf16_round)
+        stats["residual_exact"] = float((got_res[valid] == ref["residual_out"][valid]).mean())
+    else:
+        ok = np.abs(gr - z) <= err_z + U_half(z)
+        stats["residual_exact"] = float((got_res[valid] == ref["residual_out"][valid]).mean())
+    assert ok.all(), f"residual_out outside bound at {np.argwhere(~ok)[:5].tolist()}"
+
+    # ---- normalised output
+    go = got_out[valid]
+    if quant == QUANT_NONE:
+        g = _host_f64(go)
+        rnd = bf16_round if out_dtype == torch.bfloat16 else (lambda t: t.astype(np.float32).astype(np.float64))
+        ok = within_rounding(g, y - err_y, y + err_y, rnd)
+        assert ok.all(), f"out outside bound at {np.argwhere(~ok)[:5].tolist()}"
+        assert (np.abs(g - y) <= 1e-3 + 2.0 ** -7 * np.abs(y)).all(), "out outside 1e-3 + 2^-7|y|"
+        stats["out_exact"] = float((go == ref["out"][valid]).mean())
+    else:
+        if quant == QUANT_STATIC_TENSOR:
+            sc = np.full(len(vr), np.float64(np.float32(static_scale)))
+        else:
+            sc_gpu = scale_t.cpu().numpy()[vr].astype(np.float64)
+            sc_ref = ref["out_scale"][valid].astype(np.float64)
+            rel = np.abs(sc_gpu - sc_ref) / np.maximum(sc_ref, 1e-30)
+            assert (rel <= 1e-5).all(), f"per-token scale off by {rel.max():.3g}"
+            assert (rel <= 2.0 ** -16).all(), f"per-token scale off by {rel.max():.3g}"
+            stats["scale_max_rel"] = float(rel.max())
+            sc = sc_gpu
+        t = y / sc[:, None]
+        err_t = err_y / sc[:, None] + 2.0 ** -21 * np.abs(t)
+        g = e4m3_decode(go)
+        ok = within_rounding(g, t - err_t, t + err_t, e4m3_round)
+        assert ok.all(), f"e4m3 codes outside bound at {np.argwhere(~ok)[:5].tolist()}"
+        own = ref["out"][valid]
+        diff = go != own
+        both_zero = (e4m3_decode(own) == 0) & (g == 0)
+        diff &= ~both_zero
+        stats["codes_exact"] = 1.0 - float(diff.mean())
+        assert diff.mean() <= 1e-3, f"{diff.mean():.3%} of codes differ from the oracle's"
+        if diff.any():
+            steps = np.abs(g[diff] - e4m3_decode(own[diff]))
+            assert (steps <= 2 * np.abs(e4m3_step_of(e4m3_decode(own[diff])))).all()
+    # bf16 roundings of fp32 and fp64 values differ only next to a rounding tie
+    checks = []
+    if w.act_dtype == torch.bfloat16:
+        checks.append("residual_exact")
+    if quant == QUANT_NONE and out_dtype == torch.bfloat16:
+        checks.append("out_exact")
+    for key in checks:
+        assert stats[key] >= require_exact_frac, f"{key}={stats[key]}"
+    return Result(rows, v, stats)
+
+
+def U_half(z):
+    return 2.0 ** -24 * np.abs(z)
+
+
+def e4m3_step_of(v):
+    a = np.minimum(np.abs(v), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (e - 3)

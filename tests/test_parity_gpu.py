@@ -1,0 +1,316 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle on MI355X.
+
+Every test prints the case it runs (workload, rank, shape) before touching
+the GPU.  Small workloads are compared on every row of every rank; the large
+ones (C4, C5) at their full size on sampled rows, in the launch
+configuration the benchmark times.
+"""
+
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import reduce_add_rmsnorm_amd as sp
+from helpers import bf16_bits_to_f64, e4m3_decode, to_host
+from parity import run_case
+from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR,
+                                           WORKLOADS, make_inputs)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sp.load()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def sample_rows(S, v, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(S, size=min(n, S), replace=False).tolist())
+    rows |= {0, S - 1, max(v - 1, 0), min(v, S - 1)}
+    return sorted(rows)
+
+
+def c4_static_scale():
+    path = os.path.join(GOLDEN, "c4_static_scale.json")
+    with open(path) as f:
+        return float(json.load(f)["scale"])
+
+
+# ------------------------------------------------------------- workloads
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_c1_all_rows(dev, rank):
+    w = WORKLOADS["C1"]
+    say(f"C1 rank {rank}: tp={w.tp} S={w.shard_rows} H={w.hidden} f32 in, replicated residual")
+    r = run_case(w, rank, dev=dev)
+    say(r.stats)
+
+
+@pytest.mark.parametrize("rank", range(8))
+def test_c2_every_rank(dev, rank):
+    w = WORKLOADS["C2"]
+    say(f"C2 rank {rank}: tp=8 T=1000 T_pad=1024 S=128 H=4096")
+    r = run_case(w, rank, dev=dev)
+    assert r.valid == max(0, min(128, 1000 - rank * 128))
+    say(r.stats)
+
+
+@pytest.mark.parametrize("rank", range(16))
+def test_c3_every_rank(dev, rank):
+    w = WORKLOADS["C3"]
+    say(f"C3 rank {rank}: tp=16 T=3500 T_pad=3504 S=219 H=8192 bias")
+    r = run_case(w, rank, dev=dev)
+    assert r.valid == (215 if rank == 15 else 219)
+    say(r.stats)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_c4_full_size_sampled_rows(dev, rank):
+    w = WORKLOADS["C4"]
+    say(f"C4 rank {rank}: tp=8 S=8192 H=7168 static e4m3, sampled rows")
+    r = run_case(w, rank, dev=dev, rows=sample_rows(w.shard_rows, w.shard_rows, seed=rank),
+                 static_scale=c4_static_scale(), pad_fill=None)
+    say(r.stats)
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_c5_full_size_sampled_rows(dev, rank):
+    w = WORKLOADS["C5"]
+    say(f"C5 rank {rank}: tp=4 S=32768 H=5120 deepstack + dynamic e4m3, sampled rows")
+    r = run_case(w, rank, dev=dev, rows=sample_rows(w.shard_rows, w.shard_rows, seed=10 + rank),
+                 pad_fill=None)
+    say(r.stats)
+
+
+# ------------------------------------------------------------ edge cases
+
+
+def variant(name, **kw):
+    return dataclasses.replace(WORKLOADS[name], **kw)
+
+
+@pytest.mark.parametrize("H", [8, 520, 4104, 16384, 32768])
+def test_ragged_and_large_hidden(dev, H):
+    # H not a multiple of the workgroup's vector span (dead lanes), and the
+    # 4- and 8-vectors-per-thread shapes; tp=8 with runtime partial groups
+    w = variant("C2", hidden=H, num_tokens=8 * 6 - 3, num_tokens_pad=8 * 6)
+    say(f"ragged H={H} tp=8 S=6 rank 7 (3 padding rows)")
+    run_case(w, 7, dev=dev)
+
+
+@pytest.mark.parametrize("tp", [1, 3, 5, 16, 64])
+def test_partial_counts(dev, tp):
+    w = variant("C3", tp=tp, num_tokens=tp * 5 - 2, num_tokens_pad=tp * 5, hidden=1024)
+    say(f"tp={tp} S=5 H=1024 rank {tp - 1}")
+    run_case(w, tp - 1, dev=dev)
+    run_case(w, 0, dev=dev)
+
+
+@pytest.mark.parametrize("quant", [QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN])
+@pytest.mark.parametrize("pt,at", [(torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16),
+                                   (torch.float32, torch.float32)])
+def test_dtype_mixes(dev, quant, pt, at):
+    out = torch.bfloat16 if quant == QUANT_NONE else torch.uint8
+    w = variant("C5", partial_dtype=pt, act_dtype=at, quant_mode=quant, out_dtype=out,
+                num_tokens=4 * 24 - 7, num_tokens_pad=4 * 24, hidden=2048, bias=True)
+    say(f"dtypes partial={pt} act={at} quant={quant} S=24 H=2048 deepstack + bias")
+    run_case(w, 3, dev=dev, static_scale=0.01)
+
+
+def test_f32_output(dev):
+    w = variant("C2", out_dtype=torch.float32, num_tokens=1000, hidden=4096)
+    say("C2 shape, f32 out, rank 7")
+    run_case(w, 7, dev=dev)
+
+
+def test_dynamic_with_bias_two_reductions(dev):
+    w = variant("C5", bias=True, num_tokens=4 * 64, num_tokens_pad=4 * 64)
+    say("dynamic e4m3 with bias: S=64 H=5120 rank 2")
+    run_case(w, 2, dev=dev)
+
+
+def test_in_place_replicated_residual(dev):
+    w = variant("C2", residual_replicated=True, num_tokens=1000)
+    say("in-place update of a replicated residual, C2 shape, rank 7 and rank 3")
+    run_case(w, 7, dev=dev, in_place=True)
+    run_case(w, 3, dev=dev, in_place=True)
+
+
+def test_in_place_shard_residual_fp8(dev):
+    w = variant("C5", num_tokens=4 * 40, num_tokens_pad=4 * 40)
+    say("in-place shard residual, dynamic e4m3, S=40")
+    run_case(w, 1, dev=dev, in_place=True)
+
+
+def test_shard_sized_deepstack(dev):
+    w = variant("C5", num_tokens=4 * 32 - 9, num_tokens_pad=4 * 32)
+    say("deepstack passed as the shard block [S, H], rank 3 with 9 padding rows")
+    run_case(w, 3, dev=dev, shard_deepstack=True)
+
+
+def test_static_saturation(dev):
+    w = variant("C4", num_tokens=8 * 16, num_tokens_pad=8 * 16)
+    say("static e4m3 with half the calibrated scale: saturation at +-448")
+    x = make_inputs(w, rank=7, device=dev, shard_rows=16)
+    h = {k: to_host(t) for k, t in x.items()}
+    ref = oracle.reduce_add_rmsnorm(h["partials"], h["residual"], h["weight"], None, w.eps,
+                                    QUANT_NONE, None, tp_rank=7, num_tokens=w.num_tokens,
+                                    out_dtype=oracle.ORC_F32)
+    s = float(np.float32(np.abs(ref["y"]).max() / 448.0))
+    r = run_case(w, 7, dev=dev, static_scale=s, inputs={k: t.clone() if t is not None else None
+                                                       for k, t in x.items()})
+    say("calibrated", r.stats)
+    r = run_case(w, 7, dev=dev, static_scale=s / 2,
+                 inputs={k: t.clone() if t is not None else None for k, t in x.items()})
+    say("half scale", r.stats)
+
+
+def test_single_row_and_all_padding(dev):
+    w = variant("C3", num_tokens=16 * 1, num_tokens_pad=16 * 1)
+    say("S=1 shard, tp=16")
+    run_case(w, 5, dev=dev)
+    w = variant("C3", num_tokens=3 * 7, num_tokens_pad=16 * 7)
+    say("rank with no valid row (v=0): all zeros")
+    r = run_case(w, 9, dev=dev)
+    assert r.valid == 0
+
+
+def test_empty_shard_is_a_no_op(dev):
+    w = WORKLOADS["C2"]
+    x = make_inputs(w, rank=0, device=dev, shard_rows=0)
+    out = torch.empty((0, w.hidden), dtype=torch.bfloat16, device=dev)
+    say("S=0: nothing enqueued")
+    sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], None, w.eps, QUANT_NONE,
+                             None, out, None, tp_rank=0, num_tokens=0)
+    torch.cuda.synchronize()
+
+
+def test_dynamic_zero_row(dev):
+    w = variant("C5", deepstack=False, num_tokens=4 * 4, num_tokens_pad=4 * 4, hidden=512)
+    x = make_inputs(w, rank=0, device=dev, shard_rows=4)
+    x["partials"][:, 2] = 0
+    x["residual"][2] = 0
+    say("dynamic e4m3, one all-zero valid row: scale 0 and zero codes")
+    run_case(w, 0, dev=dev, inputs=x)
+    out = torch.empty((4, 512), dtype=torch.uint8, device=dev)
+    sc = torch.empty((4,), dtype=torch.float32, device=dev)
+    sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], None, w.eps,
+                             QUANT_DYNAMIC_TOKEN, None, out, sc, tp_rank=0, num_tokens=16,
+                             residual_out=torch.empty_like(x["residual"]))
+    torch.cuda.synchronize()
+    assert sc[2].item() == 0.0 and not out[2].any()
+
+
+def test_repeat_calls_are_bit_identical(dev):
+    w = WORKLOADS["C3"]
+    x = make_inputs(w, rank=15, device=dev)
+    say("C3 rank 15 twice: identical bits")
+    outs = []
+    for _ in range(2):
+        out = torch.empty((219, 8192), dtype=torch.bfloat16, device=dev)
+        ro = torch.empty((219, 8192), dtype=torch.bfloat16, device=dev)
+        sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], w.eps,
+                                 QUANT_NONE, None, out, None, tp_rank=15, num_tokens=3500,
+                                 residual_out=ro)
+        outs.append((out.clone(), ro.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+def test_invalid_call_writes_nothing(dev):
+    w = WORKLOADS["C2"]
+    x = make_inputs(w, rank=0, device=dev, shard_rows=8)
+    out = torch.full((8, w.hidden), 7.0, dtype=torch.bfloat16, device=dev)
+    say("invalid call (dynamic per-tensor quant mode 3): error, no write")
+    with pytest.raises(sp.SprmsError) as e:
+        sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], None, w.eps, 3, None,
+                                 out, None, tp_rank=0, num_tokens=64)
+    assert e.value.status == sp.SP_ERR_UNSUPPORTED
+    with pytest.raises(sp.SprmsError) as e:
+        sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], None, w.eps,
+                                 QUANT_NONE, None, out, None, tp_rank=8, num_tokens=64)
+    assert e.value.status == sp.SP_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert (out.float() == 7.0).all()
+
+
+# ---------------------------------------------- conversion sweeps (exact)
+
+
+def _conversion_call(dev, values: np.ndarray, quant):
+    """Route fp32 values through the kernel so that y equals them exactly:
+    f32 activations, tp=1 partials of +-1 with zero residual give z = +-1,
+    mean z^2 = 1 and (eps = 0) rstd = 1, so y = (+-1 * w) * 1 = +-w exactly;
+    a static scale of 1 then makes the e4m3 codes those of y."""
+    H = values.shape[0]
+    assert H % 8 == 0 and H <= 32768
+    rng = np.random.default_rng(H)
+    sign = np.where(rng.random(H) < 0.5, -1.0, 1.0).astype(np.float32)
+    P = torch.from_numpy(sign.reshape(1, 1, H)).to(dev)
+    R = torch.zeros((1, H), dtype=torch.float32, device=dev)
+    wt = torch.from_numpy(np.ascontiguousarray(values.astype(np.float32) * sign)).to(dev)
+    if quant == QUANT_STATIC_TENSOR:
+        out = torch.empty((1, H), dtype=torch.uint8, device=dev)
+        sc = torch.ones((1,), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+        sc = None
+    sp.sp_reduce_add_rmsnorm(P, R, wt, None, 0.0, quant, None, out, sc, tp_rank=0, num_tokens=1,
+                             residual_out=torch.empty_like(R))
+    torch.cuda.synchronize()
+    return to_host(out)[0]
+
+
+def test_e4m3_conversion_sweep_exact(dev):
+    # every e4m3 value, every midpoint (ties), their fp32 neighbours, a dense
+    # random sweep and out-of-range values: codes must equal the oracle's
+    # brute-force encoder bit for bit (the hardware conversion after the clamp)
+    say("e4m3 conversion sweep through the static path")
+    v = e4m3_decode(np.arange(0x7F))
+    mids = (v[:-1] + v[1:]) / 2
+    base = np.concatenate([v, -v, mids, -mids]).astype(np.float32)
+    near = np.concatenate([np.nextafter(base, np.float32(1e9)), np.nextafter(base, np.float32(-1e9))])
+    rng = np.random.default_rng(0)
+    rand = np.concatenate([rng.uniform(-460, 460, 200000), rng.normal(0, 0.02, 100000),
+                           [500.0, -500.0, 1e30, -1e30, 449.0, 464.0, 2.0 ** -12]]).astype(np.float32)
+    allv = np.concatenate([base, near, rand])
+    pad = (-len(allv)) % 32768
+    allv = np.concatenate([allv, np.zeros(pad, np.float32)])
+    for chunk in allv.reshape(-1, 32768):
+        got = _conversion_call(dev, chunk, QUANT_STATIC_TENSOR)
+        want = oracle.e4m3_from_double_array(chunk.astype(np.float64))
+        gz = (got & 0x7F) == 0
+        wz = (want & 0x7F) == 0
+        np.testing.assert_array_equal(np.where(gz & wz, 0, got), np.where(gz & wz, 0, want))
+
+
+def test_bf16_conversion_sweep_exact(dev):
+    say("bf16 conversion sweep through the bf16 output path")
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, 400000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 1e38) & (np.abs(x) > 1e-37)]
+    ties = ((rng.integers(0x0080, 0x7F00, 50000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    allv = np.concatenate([x, ties, -ties]).astype(np.float32)
+    pad = (-len(allv)) % 32768
+    allv = np.concatenate([allv, np.ones(pad, np.float32)])
+    for chunk in allv.reshape(-1, 32768):
+        got = _conversion_call(dev, chunk, QUANT_NONE)
+        want = oracle.bf16_from_double_array(chunk.astype(np.float64))
+        np.testing.assert_array_equal(got, want)
