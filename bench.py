@@ -126,6 +126,24 @@ def cpu_baseline(w, x, budget_s: float):
     }
 
 
+def copy_calibration(args, dev):
+    """A device-to-device copy of known size: every launch reads and writes
+    exactly n bytes, which fixes the scale of FETCH_SIZE / WRITE_SIZE."""
+    n = args.copy_calibration << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000 / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "gbs": round(2 * n / ms / 1e6, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,15 +152,21 @@ def main():
     ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the path, time a plain device copy of MIB MiB (the "
+                         "reference kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused shard kernel runs on one rank's shard "
               "and no collective is part of this build; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(args, dev)
+        return
+    w = WORKLOADS[args.workload]
     sp.load()
     x, launch, _ = setup(w, dev)
     stream = torch.cuda.current_stream(dev)
@@ -153,22 +177,34 @@ def main():
         launch()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: K back-to-back launches, HIP events on the launch stream
+    # at both ends, host clock between two synchronisations
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    ev0.record(stream)
+    for _ in range(args.steps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # launch-duration spread from a short pass with an event pair per launch
+    n_spread = min(args.steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+    for i in range(n_spread):
         starts[i].record(stream)
         launch()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
 
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1000.0 / args.steps
     nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step / 1000.0) / 1e9
-    avg_ms = statistics.fmean(per_launch_ms)
     achieved = nbytes / (avg_ms / 1000.0) / 1e9
     traffic = measured_traffic(w.name)
     v = w.valid_rows()
@@ -197,7 +233,7 @@ def main():
         "shard_tokens_per_s": round(v / (ms_per_step / 1000.0), 1),
         "kernel_us": {
             "mean": round(avg_ms * 1000, 2),
-            "median": round(statistics.median(per_launch_ms) * 1000, 2),
+            "median_single": round(statistics.median(per_launch_ms) * 1000, 2),
             "p10": round(float(np.percentile(per_launch_ms, 10)) * 1000, 2),
             "p90": round(float(np.percentile(per_launch_ms, 90)) * 1000, 2),
         },

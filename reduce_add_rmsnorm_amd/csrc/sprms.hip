@@ -6,27 +6,32 @@
 // pages that define it.  This file is the implementation: host-side
 // validation and dispatch behind the C ABI, and one family of kernels.
 //
-// Kernel design (HBM-bandwidth bound: ~1 flop per byte, no dense
+// Kernel design (HBM-bandwidth bound: about one flop per byte and no dense
 // contraction, so no MFMA):
 //   * one workgroup per shard row; the row is split into 8-element vectors
-//     (16 B of bf16), thread t owns vectors t, t+NT, ..., t+(VPT-1)NT, so
-//     every load and store instruction of a wavefront covers 1 KiB of
-//     contiguous memory;
-//   * every input vector of the row (tp partials, deepstack, residual, gain,
-//     bias) is loaded into registers before the first add, so each thread has
-//     tp*VPT + 2..4 x VPT 16-byte loads in flight; the sum stays in fp32
-//     registers and nothing is re-read from HBM;
-//   * the updated residual is written once, straight after the adds;
-//   * sum of squares (and, for per-token FP8 without bias, max |z*w|) are
+//     (16 B of bf16) and thread t owns vectors t, t+NT, ..., so each load or
+//     store instruction of a wavefront covers 1 KiB of contiguous memory.
+//     Rows of up to 8192 elements use one vector per thread (up to 1024
+//     threads); longer rows use 4 or 8 vectors per thread within 512 threads;
+//   * all row data moves through buffer instructions on per-row descriptors
+//     held in scalar registers; the streamed data (partials, deepstack,
+//     residual, outputs) is marked non-temporal, the gain and bias are
+//     cached (every row re-reads them from L2);
+//   * every load of the row is issued before the first add when the loads
+//     fit the register budget (otherwise partials come in groups of 2-4);
+//     the fp32 sum stays in registers and nothing is re-read;
+//   * the updated residual is stored as soon as the sum is known, which
+//     spreads the write traffic over the kernel;
+//   * the sum of squares (and, for per-token FP8 without bias, max |z*w|) is
 //     reduced with DPP row operations inside the wavefront, then across
-//     wavefronts through LDS with a single barrier; with a bias the per-token
-//     max needs y, so a second LDS step follows;
+//     wavefronts through LDS with one barrier; with a bias the per-token max
+//     needs y, so a second LDS step follows;
 //   * output conversion uses gfx950's v_cvt_pk_bf16_f32 / v_cvt_pk_fp8_f32
 //     (OCP e4m3fn), after an explicit clamp to +-448;
 //   * padding rows (s >= valid_rows) only store zeros.
 // Rows are independent and there is no reuse across rows except the gain and
-// bias vectors (a few KiB, served from L2), so the workgroup -> row mapping
-// needs no XCD-aware swizzle.
+// bias vectors (a few KiB, served from each XCD's L2), so the workgroup ->
+// row mapping needs no XCD-aware swizzle.
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -39,9 +44,18 @@
 namespace {
 
 constexpr int kVec = 8;  // elements per thread-vector
-constexpr int kMaxThreads = 512;  // workgroup size bound (8 wavefronts)
+// Workgroup size bounds: one 8-element vector per thread allows a
+// 1024-thread workgroup (rows of up to 8192 elements); more vectors per
+// thread hold more registers and are limited to 512 threads.
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxThreadsMultiVec = 512;
 constexpr int kMaxWaves = kMaxThreads / 64;
-constexpr int kMaxHidden = kMaxThreads * 8 * kVec;  // 32768
+constexpr int kMaxHidden = 32768;
+
+template <int VPT>
+constexpr int max_threads() {
+  return VPT == 1 ? kMaxThreads : kMaxThreadsMultiVec;
+}
 
 enum OutMode { OM_BF16 = 0, OM_F32 = 1, OM_FP8_STATIC = 2, OM_FP8_DYN = 3 };
 
@@ -63,9 +77,39 @@ struct KArgs {
 };
 
 // ------------------------------------------------------------ element I/O
+//
+// All row data moves through buffer instructions.  A resource descriptor
+// covers exactly one row of one tensor (its base is uniform per workgroup,
+// so it lives in scalar registers); the per-lane operand is a 32-bit byte
+// offset inside the row.
 
+// Cache policy of the streamed (read-once / write-once) row data, as the
+// buffer instruction's cache-policy bits on gfx950: bit 0 sc0, bit 1 nt,
+// bit 4 sc1.  Gain and bias are re-read by every row and use policy 0.
+#ifndef SPRMS_STREAM_LOAD_POLICY
+#define SPRMS_STREAM_LOAD_POLICY 2
+#endif
+#ifndef SPRMS_STREAM_STORE_POLICY
+#define SPRMS_STREAM_STORE_POLICY 2
+#endif
+constexpr int kLoadPolicy = SPRMS_STREAM_LOAD_POLICY;
+constexpr int kStorePolicy = SPRMS_STREAM_STORE_POLICY;
+constexpr int kCachedPolicy = 0;
+
+// word 3 of a gfx9-family buffer descriptor: 32-bit data format, raw
+// (stride 0) addressing with the range check against num_records
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
@@ -79,69 +123,78 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 template <int DT>
 struct Vec;
 
+// 8 bf16 = one 16-byte access
 template <>
 struct Vec<SP_BF16> {
-  using raw = uint4;
-  static __device__ __forceinline__ raw load(const void* base, int64_t e) {
-    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  using raw = u32x4;
+  static constexpr int kBytes = 16;
+  template <int POL>
+  static __device__ __forceinline__ raw load(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
   }
-  static __device__ __forceinline__ void unpack(const raw& r, float (&f)[kVec]) {
-    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
-    f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
-    f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
-    f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+  static __device__ __forceinline__ void add(const raw& v, float (&f)[kVec]) {
+    f[0] += bf16_lo(v.x); f[1] += bf16_hi(v.x);
+    f[2] += bf16_lo(v.y); f[3] += bf16_hi(v.y);
+    f[4] += bf16_lo(v.z); f[5] += bf16_hi(v.z);
+    f[6] += bf16_lo(v.w); f[7] += bf16_hi(v.w);
   }
-  static __device__ __forceinline__ void add(const raw& r, float (&f)[kVec]) {
-    f[0] += bf16_lo(r.x); f[1] += bf16_hi(r.x);
-    f[2] += bf16_lo(r.y); f[3] += bf16_hi(r.y);
-    f[4] += bf16_lo(r.z); f[5] += bf16_hi(r.z);
-    f[6] += bf16_lo(r.w); f[7] += bf16_hi(r.w);
+  static __device__ __forceinline__ void unpack(const raw& v, float (&f)[kVec]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
   }
-  static __device__ __forceinline__ void store(void* base, int64_t e, const float (&f)[kVec]) {
-    uint4 o;
-    o.x = pack_bf16(f[0], f[1]);
-    o.y = pack_bf16(f[2], f[3]);
-    o.z = pack_bf16(f[4], f[5]);
-    o.w = pack_bf16(f[6], f[7]);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = o;
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[kVec]) {
+    u32x4 o = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+               pack_bf16(f[6], f[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(o, r, off, 0, kStorePolicy);
   }
-  static __device__ __forceinline__ void store_zero(void* base, int64_t e) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = make_uint4(0, 0, 0, 0);
+  static __device__ __forceinline__ void store_zero(rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, r, off, 0, kStorePolicy);
   }
 };
 
+// 8 f32 = two 16-byte accesses
 template <>
 struct Vec<SP_F32> {
   struct raw {
-    float4 a, b;
+    u32x4 a, b;
   };
-  static __device__ __forceinline__ raw load(const void* base, int64_t e) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e);
-    return raw{p[0], p[1]};
+  static constexpr int kBytes = 32;
+  template <int POL>
+  static __device__ __forceinline__ raw load(rsrc_t r, uint32_t off) {
+    return raw{__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL),
+               __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, POL)};
   }
-  static __device__ __forceinline__ void unpack(const raw& r, float (&f)[kVec]) {
-    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
-    f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  static __device__ __forceinline__ void add(const raw& v, float (&f)[kVec]) {
+    f[0] += __uint_as_float(v.a.x); f[1] += __uint_as_float(v.a.y);
+    f[2] += __uint_as_float(v.a.z); f[3] += __uint_as_float(v.a.w);
+    f[4] += __uint_as_float(v.b.x); f[5] += __uint_as_float(v.b.y);
+    f[6] += __uint_as_float(v.b.z); f[7] += __uint_as_float(v.b.w);
   }
-  static __device__ __forceinline__ void add(const raw& r, float (&f)[kVec]) {
-    f[0] += r.a.x; f[1] += r.a.y; f[2] += r.a.z; f[3] += r.a.w;
-    f[4] += r.b.x; f[5] += r.b.y; f[6] += r.b.z; f[7] += r.b.w;
+  static __device__ __forceinline__ void unpack(const raw& v, float (&f)[kVec]) {
+    f[0] = __uint_as_float(v.a.x); f[1] = __uint_as_float(v.a.y);
+    f[2] = __uint_as_float(v.a.z); f[3] = __uint_as_float(v.a.w);
+    f[4] = __uint_as_float(v.b.x); f[5] = __uint_as_float(v.b.y);
+    f[6] = __uint_as_float(v.b.z); f[7] = __uint_as_float(v.b.w);
   }
-  static __device__ __forceinline__ void store(void* base, int64_t e, const float (&f)[kVec]) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + e);
-    p[0] = make_float4(f[0], f[1], f[2], f[3]);
-    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const float (&f)[kVec]) {
+    u32x4 lo = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                __float_as_uint(f[3])};
+    u32x4 hi = {__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                __float_as_uint(f[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(lo, r, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(hi, r, off + 16, 0, kStorePolicy);
   }
-  static __device__ __forceinline__ void store_zero(void* base, int64_t e) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + e);
-    p[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    p[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  static __device__ __forceinline__ void store_zero(rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, r, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0, 0, 0, 0}, r, off + 16, 0, kStorePolicy);
   }
 };
 
 // 8 fp32 -> 8 OCP e4m3fn codes (little-endian byte order = element order),
 // clamped to +-448 first so the conversion never sees an out-of-range value.
-__device__ __forceinline__ uint2 pack_e4m3(const float (&t)[kVec]) {
+__device__ __forceinline__ u32x2 pack_e4m3(const float (&t)[kVec]) {
   float c[kVec];
 #pragma unroll
   for (int k = 0; k < kVec; ++k) c[k] = fminf(fmaxf(t[k], -448.0f), 448.0f);
@@ -149,7 +202,11 @@ __device__ __forceinline__ uint2 pack_e4m3(const float (&t)[kVec]) {
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-  return make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+  return u32x2{static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+}
+
+__device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
 }
 
 // ------------------------------------------------------------- reductions
@@ -189,43 +246,44 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ----------------------------------------------------------------- kernel
 
-// PT: partial dtype, AT: activation dtype, OM: output mode,
-// TP: number of partials (0 = runtime, loaded in groups of 4),
-// VPT: 8-element vectors per thread.
+// One shard row s, processed by the whole workgroup.
 template <int PT, int AT, int OM, int TP, int VPT>
-__global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
+__device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, float (&red)[3][kMaxWaves]) {
   using VP = Vec<PT>;
   using VA = Vec<AT>;
-  __shared__ float red[3][kMaxWaves];
+  constexpr int kOutBytes = OM == OM_F32 ? 32 : OM == OM_BF16 ? 16 : 8;  // per 8 elements
 
-  const int64_t s = blockIdx.x;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int nw = nt >> 6;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int64_t row = s * a.H;
+  const int64_t row = s * a.H;  // element index of the row's first element
+  const uint32_t rowA = static_cast<uint32_t>(a.H) * (VA::kBytes / kVec);
+  const uint32_t rowO = static_cast<uint32_t>(a.H) * kOutBytes / kVec;
 
   // Lanes past the end of the row (only when NT*VPT*8 > H) load a valid
-  // element of the row and discard it; they store nothing and add 0.
-  int64_t col[VPT];
+  // vector of the row and discard it; they store nothing and add 0.
+  uint32_t vec[VPT];
   bool live[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int j = tid + i * nt;
     live[i] = j < a.nvec;
-    col[i] = static_cast<int64_t>(live[i] ? j : a.nvec - 1) * kVec;
+    vec[i] = static_cast<uint32_t>(live[i] ? j : a.nvec - 1);
   }
+
+  const rsrc_t r_res_out = row_rsrc(static_cast<char*>(a.residual_out) + row * (VA::kBytes / kVec), rowA);
+  const rsrc_t r_out = row_rsrc(static_cast<char*>(a.out) + row * kOutBytes / kVec, rowO);
 
   if (s >= a.valid) {  // padding row: zeros only, no input is read
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       if (!live[i]) continue;
-      VA::store_zero(a.residual_out, row + col[i]);
-      if constexpr (OM == OM_BF16) Vec<SP_BF16>::store_zero(a.out, row + col[i]);
-      if constexpr (OM == OM_F32) Vec<SP_F32>::store_zero(a.out, row + col[i]);
-      if constexpr (OM == OM_FP8_STATIC || OM == OM_FP8_DYN)
-        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.out) + row + col[i]) = make_uint2(0, 0);
+      VA::store_zero(r_res_out, vec[i] * VA::kBytes);
+      if constexpr (OM == OM_BF16) Vec<SP_BF16>::store_zero(r_out, vec[i] * 16);
+      if constexpr (OM == OM_F32) Vec<SP_F32>::store_zero(r_out, vec[i] * 32);
+      if constexpr (OM == OM_FP8_STATIC || OM == OM_FP8_DYN) store_e4m3(r_out, vec[i] * 8, u32x2{0, 0});
     }
     if constexpr (OM == OM_FP8_DYN) {
       if (tid == 0) a.out_scale[s] = 0.0f;
@@ -235,33 +293,48 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
 
   const bool has_ds = a.deepstack != nullptr;
   const bool has_bias = a.bias != nullptr;
+  const rsrc_t r_w = row_rsrc(a.weight, rowA);
+  const rsrc_t r_b = row_rsrc(a.bias, rowA);
+  const rsrc_t r_res = row_rsrc(static_cast<const char*>(a.residual) + row * (VA::kBytes / kVec), rowA);
+  const rsrc_t r_ds = row_rsrc(static_cast<const char*>(a.deepstack) + row * (VA::kBytes / kVec), rowA);
+  const uint32_t rowP = static_cast<uint32_t>(a.H) * (VP::kBytes / kVec);
+  const char* p0 = static_cast<const char*>(a.partials) + row * (VP::kBytes / kVec);
+  const int64_t planeB = a.plane * (VP::kBytes / kVec);
+
   float z[VPT][kVec];
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
 #pragma unroll
     for (int k = 0; k < kVec; ++k) z[i][k] = 0.0f;
 
+  // Gain and bias first: vmcnt counts loads and stores in issue order, so the
+  // oldest loads can be waited for without waiting for later stores.
   typename VA::raw rw[VPT], rb[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) rw[i] = VA::template load<kCachedPolicy>(r_w, vec[i] * VA::kBytes);
+  if (has_bias) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) rb[i] = VA::template load<kCachedPolicy>(r_b, vec[i] * VA::kBytes);
+  }
+  float static_scale = 1.0f;
+  if constexpr (OM == OM_FP8_STATIC) static_scale = a.out_scale[0];
+
   if constexpr (TP > 0) {
     // ---- every load of the row in flight before the first add
     typename VP::raw rp[TP][VPT];
     typename VA::raw rd[VPT], rr[VPT];
 #pragma unroll
-    for (int q = 0; q < TP; ++q)
+    for (int q = 0; q < TP; ++q) {
+      const rsrc_t r_p = row_rsrc(p0 + q * planeB, rowP);
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) rp[q][i] = VP::load(a.partials, q * a.plane + row + col[i]);
+      for (int i = 0; i < VPT; ++i) rp[q][i] = VP::template load<kLoadPolicy>(r_p, vec[i] * VP::kBytes);
+    }
     if (has_ds) {
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) rd[i] = VA::load(a.deepstack, row + col[i]);
+      for (int i = 0; i < VPT; ++i) rd[i] = VA::template load<kLoadPolicy>(r_ds, vec[i] * VA::kBytes);
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) rr[i] = VA::load(a.residual, row + col[i]);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) rw[i] = VA::load(a.weight, col[i]);
-    if (has_bias) {
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) rb[i] = VA::load(a.bias, col[i]);
-    }
+    for (int i = 0; i < VPT; ++i) rr[i] = VA::template load<kLoadPolicy>(r_res, vec[i] * VA::kBytes);
     // sum of partials in ascending rank order, then deepstack, then residual
 #pragma unroll
     for (int q = 0; q < TP; ++q)
@@ -284,9 +357,9 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
 #pragma unroll
       for (int k = 0; k < G; ++k)
         if (k < g) {
+          const rsrc_t r_p = row_rsrc(p0 + (q0 + k) * planeB, rowP);
 #pragma unroll
-          for (int i = 0; i < VPT; ++i)
-            rp[k][i] = VP::load(a.partials, (q0 + k) * a.plane + row + col[i]);
+          for (int i = 0; i < VPT; ++i) rp[k][i] = VP::template load<kLoadPolicy>(r_p, vec[i] * VP::kBytes);
         }
 #pragma unroll
       for (int k = 0; k < G; ++k)
@@ -297,22 +370,18 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
     }
     if (has_ds) {
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) VA::add(VA::load(a.deepstack, row + col[i]), z[i]);
+      for (int i = 0; i < VPT; ++i)
+        VA::add(VA::template load<kLoadPolicy>(r_ds, vec[i] * VA::kBytes), z[i]);
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) VA::add(VA::load(a.residual, row + col[i]), z[i]);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) rw[i] = VA::load(a.weight, col[i]);
-    if (has_bias) {
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) rb[i] = VA::load(a.bias, col[i]);
-    }
+    for (int i = 0; i < VPT; ++i)
+      VA::add(VA::template load<kLoadPolicy>(r_res, vec[i] * VA::kBytes), z[i]);
   }
 
-  // ---- store the updated residual once
+  // ---- store the updated residual once, as soon as it is known
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
-    if (live[i]) VA::store(a.residual_out, row + col[i], z[i]);
+    if (live[i]) VA::store(r_res_out, vec[i] * VA::kBytes, z[i]);
 
   // ---- zw = z * w; per-thread sum of z^2 and max |zw|
   float ss = 0.0f, amax = 0.0f;
@@ -359,14 +428,14 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
   }
 
   if constexpr (OM == OM_BF16 || OM == OM_F32) {
+    using VO = Vec<OM == OM_BF16 ? SP_BF16 : SP_F32>;
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (live[i]) Vec<OM == OM_BF16 ? SP_BF16 : SP_F32>::store(a.out, row + col[i], z[i]);
-    return;
+      if (live[i]) VO::store(r_out, vec[i] * VO::kBytes, z[i]);
   } else {
     float inv;
     if constexpr (OM == OM_FP8_STATIC) {
-      inv = 1.0f / a.out_scale[0];
+      inv = 1.0f / static_scale;
     } else {
       // max |y|: without bias, rounding is monotone so max|zw*rstd| equals
       // max|zw| * rstd exactly; with bias it needs a pass over y.
@@ -396,10 +465,18 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
       float t[kVec];
 #pragma unroll
       for (int k = 0; k < kVec; ++k) t[k] = z[i][k] * inv;
-      if (live[i])
-        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.out) + row + col[i]) = pack_e4m3(t);
+      if (live[i]) store_e4m3(r_out, vec[i] * 8, pack_e4m3(t));
     }
   }
+}
+
+// PT: partial dtype, AT: activation dtype, OM: output mode,
+// TP: number of partials (0 = runtime, loaded in groups),
+// VPT: 8-element vectors per thread.  One workgroup per shard row.
+template <int PT, int AT, int OM, int TP, int VPT>
+__global__ void __launch_bounds__(max_threads<VPT>()) sprms_kernel(const KArgs a) {
+  __shared__ float red[3][kMaxWaves];
+  process_row<PT, AT, OM, TP, VPT>(a, blockIdx.x, red);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -407,11 +484,13 @@ __global__ void __launch_bounds__(kMaxThreads) sprms_kernel(const KArgs a) {
 using KFn = void (*)(KArgs);
 
 // A compile-time partial count (every load in flight at once) is used while
-// the row's loads fit in about 112 VGPRs; otherwise the grouped path.
+// the row's loads fit in the register budget of the workgroup size (about 96
+// VGPRs at 1024 threads, 112 at 512); otherwise the grouped path.
 template <int PT, int AT, int TP, int VPT>
 constexpr int fixed_tp() {
   constexpr int rp = PT == SP_F32 ? 8 : 4, ra = AT == SP_F32 ? 8 : 4;
-  return (TP * VPT * rp + 4 * VPT * ra <= 112) ? TP : 0;
+  constexpr int budget = VPT == 1 ? 96 : 112;
+  return (TP * VPT * rp + 4 * VPT * ra <= budget) ? TP : 0;
 }
 
 template <int PT, int AT, int OM, int TP>
@@ -455,11 +534,11 @@ KFn pick_kernel(int pt, int at, int om, int tp, int vpt) {
   return nullptr;
 }
 
-// Threads per row: the fewest 8-element vectors per thread (1, 2, 4, 8) that
-// keep the workgroup at <= 512 threads, rounded up to whole wavefronts.
+// Threads per row: one 8-element vector per thread while the row has at most
+// 1024 vectors (H <= 8192), else 4 or 8 vectors per thread within 512
+// threads; rounded up to whole wavefronts.
 void launch_shape(int nvec, int* vpt, int* nt) {
-  int v = 1;
-  while (v < 8 && (nvec + v - 1) / v > kMaxThreads) v *= 2;
+  const int v = nvec <= kMaxThreads ? 1 : (nvec + 3) / 4 <= kMaxThreadsMultiVec ? 4 : 8;
   int n = (nvec + v - 1) / v;
   n = (n + 63) / 64 * 64;
   *vpt = v;
@@ -630,6 +709,8 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
                                                         : OM_F32;
   int vpt, nt;
   launch_shape(ka.nvec, &vpt, &nt);
+  if (nt > (vpt == 1 ? kMaxThreads : kMaxThreadsMultiVec) || nt % 64 != 0)  // launch bounds, LDS
+    return fail(SP_ERR_UNSUPPORTED, "no launch shape for hidden=%lld", (long long)H);
   KFn fn = pick_kernel(p->partial_dtype, p->act_dtype, om, p->tp, vpt);
   if (!fn) return fail(SP_ERR_UNSUPPORTED, "no kernel for this dtype / mode combination");
   void* args[] = {&ka};

@@ -176,9 +176,12 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
             assert (rel <= 2.0 ** -16).all(), f"per-token scale off by {rel.max():.3g}"
             stats["scale_max_rel"] = float(rel.max())
             sc = sc_gpu
-        t = y / sc[:, None]
-        err_t = err_y / sc[:, None] + 2.0 ** -21 * np.abs(t)
         g = e4m3_decode(go)
+        zero = sc == 0  # a row whose max |y| is 0: scale 0 and zero codes
+        assert not g[zero].any(), "non-zero codes on a row with scale 0"
+        sc_safe = np.where(zero, 1.0, sc)[:, None]
+        t = np.where(zero[:, None], 0.0, y / sc_safe)
+        err_t = np.where(zero[:, None], 0.0, err_y / sc_safe + 2.0 ** -21 * np.abs(t))
         ok = within_rounding(g, t - err_t, t + err_t, e4m3_round)
         assert ok.all(), f"e4m3 codes outside bound at {np.argwhere(~ok)[:5].tolist()}"
         own = ref["out"][valid]
