@@ -79,6 +79,30 @@ def setup(w, dev):
     return x, launch, (out, res_out, scale)
 
 
+def setup_gather(w, dev):
+    """Every rank's shard output of the workload (S x H in the output dtype,
+    plus per-row scales for quantised outputs), gathered into [T, H]."""
+    S, H, T = w.shard_rows, w.hidden, w.num_tokens
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_index)
+    if w.out_dtype == torch.uint8:
+        shards = [torch.randint(0, 256, (S, H), generator=g, device=dev, dtype=torch.uint8)
+                  for _ in range(w.tp)]
+    else:
+        shards = [torch.randn((S, H), generator=g, device=dev).to(w.out_dtype) for _ in range(w.tp)]
+    scaled = w.quant_mode == QUANT_DYNAMIC_TOKEN
+    scales = [torch.rand(S, generator=g, device=dev) for _ in range(w.tp)] if scaled else None
+    out = torch.empty((T, H), dtype=w.out_dtype, device=dev)
+    out_scale = torch.empty((T,), dtype=torch.float32, device=dev) if scaled else None
+
+    def launch():
+        sp.sp_all_gather_unpad(shards, scales, out, out_scale, num_tokens=T)
+
+    e = out.element_size()
+    nbytes = 2 * T * (H * e + (4 if scaled else 0))  # read and write each gathered byte once
+    return (shards, scales, out, out_scale), launch, nbytes, T
+
+
 def cpu_baseline(w, x, budget_s: float):
     """The C oracle on the first rows of the same shard, single-threaded."""
     import oracle  # CPU checker; only this leg of the benchmark uses it
@@ -152,6 +176,9 @@ def main():
     ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--path", default="fused", choices=["fused", "gather"],
+                    help="fused: the shard kernel (the headline); gather: AllGather + unpad of "
+                         "every rank's shard output of the workload into [T, H] on this GPU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling hardware byte counters)")
@@ -168,7 +195,11 @@ def main():
         return
     w = WORKLOADS[args.workload]
     sp.load()
-    x, launch, _ = setup(w, dev)
+    if args.path == "gather":
+        x, launch, nbytes, tokens = setup_gather(w, dev)
+    else:
+        x, launch, _ = setup(w, dev)
+        nbytes, tokens = w.algorithmic_bytes(), w.valid_rows()
     stream = torch.cuda.current_stream(dev)
     print(f"# {w.name}: {w.description}; rank {w.rank}; S={w.shard_rows} H={w.hidden} "
           f"tp={w.tp}", file=sys.stderr, flush=True)
@@ -203,11 +234,9 @@ def main():
     per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
 
     ms_per_step = wall * 1000.0 / args.steps
-    nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step / 1000.0) / 1e9
     achieved = nbytes / (avg_ms / 1000.0) / 1e9
-    traffic = measured_traffic(w.name)
-    v = w.valid_rows()
+    traffic = measured_traffic(w.name if args.path == "fused" else f"{w.name}-gather")
 
     result = {
         "metric": METRIC,
@@ -223,14 +252,17 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: {w.description}",
+            "workload": (f"{w.name}: {w.description}" if args.path == "fused" else
+                         f"{w.name} AllGather + unpad of all {w.tp} shard outputs into "
+                         f"[{w.num_tokens}, {w.hidden}] (+ per-row scales)"),
+            "path": "sp_reduce_add_rmsnorm" if args.path == "fused" else "sp_all_gather_unpad",
             "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
             "shard_rows": w.shard_rows, "hidden": w.hidden,
             "quant": QUANT_NAMES[w.quant_mode], "deepstack": w.deepstack, "bias": w.bias,
             "algorithmic_bytes": nbytes,
         },
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "shard_tokens_per_s": round(v / (ms_per_step / 1000.0), 1),
+        "shard_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
         "kernel_us": {
             "mean": round(avg_ms * 1000, 2),
             "median_single": round(statistics.median(per_launch_ms) * 1000, 2),
@@ -247,7 +279,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and args.path == "fused":
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(result), flush=True)
 

@@ -74,7 +74,18 @@ typedef struct {
   int64_t residual_rows;  /* S (shard residual) or tp*S (replicated: block tp_rank is used) */
   int64_t deepstack_rows; /* 0 iff deepstack == NULL, else S or tp*S (block tp_rank is used) */
   void* residual_out;     /* device [S][H] act_dtype, or NULL: write the used residual rows in place */
+  int64_t partial_stride; /* elements from partial q's row s to partial q+1's row s; 0 means S*H
+                             (a packed [tp][S][H] block).  T_pad*H lets partials be the rank's
+                             row block of tp full [T_pad][H] partial tensors held in one buffer. */
+  int32_t flags;          /* 0 or SP_FLAG_VALID_ROWS_ONLY */
 } sp_problem;
+
+/* Flag: write out, out_scale and residual_out for the shard's valid rows
+ * [0, valid_rows) only and leave the padding rows untouched, so that `out`
+ * may point at row r*S of an unpadded gathered [T][H] tensor (the AllGather
+ * + unpad of FlashComm1, vllm-ascend SP / FlashComm guide, §3.3, written in
+ * place by each rank). */
+#define SP_FLAG_VALID_ROWS_ONLY 1
 
 /*
  * sp_reduce_add_rmsnorm -- enqueue the fused shard path on `stream`.
@@ -117,6 +128,41 @@ typedef struct {
 int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
                           const void* weight, const void* bias, float eps, int quant_mode,
                           const void* deepstack, void* out, float* out_scale, void* stream);
+
+/* Problem descriptor of sp_all_gather_unpad (host memory, read during the call only). */
+typedef struct {
+  int32_t tp;          /* number of shards, 1 <= tp <= 64 */
+  int32_t dtype;       /* element type of the shard outputs: SP_F32 | SP_BF16 | SP_FP8_E4M3 */
+  int64_t shard_rows;  /* S, rows per shard (padded), 0 <= S <= 2^31 - 1 */
+  int64_t hidden;      /* H, H % 8 == 0, 8 <= H <= 32768 */
+  int64_t num_tokens;  /* T, valid tokens over all shards, 0 <= T <= tp * S, T < 2^31 */
+} sp_gather_problem;
+
+/*
+ * sp_all_gather_unpad -- the AllGather + unpad that follows the shard path:
+ * shard q's rows [0, v_q), v_q = max(0, min(S, T - q*S)), become rows
+ * [q*S, q*S + v_q) of the gathered tensor; padding rows are dropped
+ * (vllm-ascend SP / FlashComm guide, §3.3, all_gather then unpad; the
+ * quantised payload and its scales are gathered together: vLLM SP / AsyncTP /
+ * quantisation notes, §4).
+ *
+ *   g             problem descriptor (host)
+ *   shards        host array of tp device pointers, shard q's output [S][H] (dtype).
+ *                 On one GPU these are local buffers; on a node they may be
+ *                 peer-mapped buffers of the other ranks (the kernel pulls).
+ *   shard_scales  host array of tp device pointers to [S] f32 per-row scales, or NULL
+ *   out           device [T][H] dtype; out and every shard 16-byte aligned when a
+ *                 row is a multiple of 16 bytes, else 8-byte aligned
+ *   out_scale     device [T] f32; required iff shard_scales != NULL
+ *   stream        hipStream_t (NULL = default stream)
+ *
+ * Bytes are copied unchanged (bit-exact).  Same error convention as
+ * sp_reduce_add_rmsnorm: every check runs before anything is enqueued, and
+ * out must not overlap a shard.  T == 0 enqueues nothing.
+ */
+int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
+                        const float* const* shard_scales, void* out, float* out_scale,
+                        void* stream);
 
 /*
  * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.

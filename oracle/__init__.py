@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     QUANT_NONE,
     QUANT_STATIC_TENSOR,
     OracleError,
+    all_gather_unpad,
     bf16_from_double,
     bf16_from_double_array,
     bf16_to_double,

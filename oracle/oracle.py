@@ -79,6 +79,9 @@ def _load():
     lib.orc_e4m3_from_double.restype = C.c_uint8
     lib.orc_e4m3_to_double.argtypes = [C.c_uint8]
     lib.orc_e4m3_to_double.restype = C.c_double
+    lib.orc_all_gather_unpad.argtypes = [i32, i64, i64, i64, i32, C.POINTER(vp), C.POINTER(vp),
+                                         vp, vp]
+    lib.orc_all_gather_unpad.restype = C.c_int
     lib.orc_bf16_from_double_n.argtypes = [vp, i64, vp]
     lib.orc_bf16_from_double_n.restype = None
     lib.orc_e4m3_from_double_n.argtypes = [vp, i64, vp]
@@ -192,3 +195,24 @@ def e4m3_from_double_array(x) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint8)
     _load().orc_e4m3_from_double_n(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def all_gather_unpad(shards, scales=None, *, num_tokens):
+    """Gather tp host shard outputs [S, H] (any 1/2/4-byte dtype) into [T, H];
+    per-row scales [S] into [T].  Returns (out, out_scale or None)."""
+    lib = _load()
+    shards = [np.ascontiguousarray(a) for a in shards]
+    tp = len(shards)
+    S, H = shards[0].shape
+    e = shards[0].dtype.itemsize
+    out = np.zeros((num_tokens, H), dtype=shards[0].dtype)
+    src = (C.c_void_p * tp)(*[a.ctypes.data for a in shards])
+    ssrc, out_scale = None, None
+    if scales is not None:
+        scales = [np.ascontiguousarray(a, dtype=np.float32) for a in scales]
+        ssrc = (C.c_void_p * tp)(*[a.ctypes.data for a in scales])
+        out_scale = np.zeros((num_tokens,), dtype=np.float32)
+    rc = lib.orc_all_gather_unpad(tp, S, H, num_tokens, e, src, ssrc, _ptr(out), _ptr(out_scale))
+    if rc != 0:
+        raise OracleError(f"orc_all_gather_unpad failed: {rc}")
+    return out, out_scale

@@ -315,3 +315,25 @@ void orc_bf16_from_double_n(const double* x, int64_t n, uint16_t* out) {
 void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_from_double(x[i]);
 }
+
+/* ------------------------------------------------------- all-gather + unpad */
+
+/* AllGather followed by unpad ([SP/FC] §3.3: gather the shards along the
+ * token dimension, then drop the padding rows): row t < T of the gathered
+ * tensor is row t - q*S of shard q = t / S.  Bytes are copied unchanged. */
+int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t H, int64_t T, int32_t elt_bytes,
+                         const void* const* shards, const float* const* scales, void* out,
+                         float* out_scale) {
+  if (tp < 1 || S < 0 || H < 1 || T < 0 || T > (int64_t)tp * S) return ORC_ERR_SHAPE;
+  if (elt_bytes != 1 && elt_bytes != 2 && elt_bytes != 4) return ORC_ERR_DTYPE;
+  if (T > 0 && (!shards || !out)) return ORC_ERR_NULL;
+  if (scales && !out_scale) return ORC_ERR_NULL;
+  const size_t row = (size_t)H * (size_t)elt_bytes;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t q = t / S;
+    const int64_t s = t - q * S;
+    memcpy((char*)out + (size_t)t * row, (const char*)shards[q] + (size_t)s * row, row);
+    if (scales) out_scale[t] = scales[q][s];
+  }
+  return ORC_OK;
+}

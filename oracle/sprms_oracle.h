@@ -86,6 +86,12 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
                            void* residual_out, void* out, float* out_scale,
                            double* z_dbg, double* y_dbg);
 
+/* AllGather + unpad of tp shard outputs [S][H] (elt_bytes each element) into
+ * out [T][H]; scales [tp][S] -> out_scale [T] when scales != NULL. */
+int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t H, int64_t T, int32_t elt_bytes,
+                         const void* const* shards, const float* const* scales, void* out,
+                         float* out_scale);
+
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
 double orc_bf16_to_double(uint16_t bits);

@@ -29,8 +29,9 @@ SP_QUANT_NONE, SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN = 0, 1, 2
 SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED, SP_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 
-EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_shard_geometry", "sp_error_string",
-            "sp_last_error")
+EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_shard_geometry",
+            "sp_error_string", "sp_last_error")
+SP_FLAG_VALID_ROWS_ONLY = 1
 
 
 class SprmsError(RuntimeError):
@@ -52,6 +53,18 @@ class sp_problem(C.Structure):
         ("residual_rows", C.c_int64),
         ("deepstack_rows", C.c_int64),
         ("residual_out", C.c_void_p),
+        ("partial_stride", C.c_int64),
+        ("flags", C.c_int32),
+    ]
+
+
+class sp_gather_problem(C.Structure):
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("dtype", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("hidden", C.c_int64),
+        ("num_tokens", C.c_int64),
     ]
 
 
@@ -76,6 +89,9 @@ def load(build_if_missing: bool = False):
     lib.sp_validate.argtypes = [C.POINTER(sp_problem), vp, vp, vp, vp, C.c_float, C.c_int, vp, vp,
                                 vp]
     lib.sp_validate.restype = C.c_int
+    lib.sp_all_gather_unpad.argtypes = [C.POINTER(sp_gather_problem), C.POINTER(vp),
+                                        C.POINTER(vp), vp, vp, vp]
+    lib.sp_all_gather_unpad.restype = C.c_int
     lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
                                       C.POINTER(i64)]
     lib.sp_shard_geometry.restype = C.c_int
@@ -113,26 +129,46 @@ def _check(status: int):
         raise SprmsError(status, sp_last_error())
 
 
-def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deepstack=None,
-                 residual_out=None) -> sp_problem:
-    """sp_problem from tensor shapes and dtypes."""
+def _partials_stride(partials) -> int:
+    """Element stride between partials; rows within a partial must be packed."""
     tp, S, H = partials.shape
+    if partials.stride(2) != 1 or (S > 1 and partials.stride(1) != H):
+        raise ValueError("partials rows must be contiguous [S][H] blocks")
+    return partials.stride(0) if tp > 1 else S * H
+
+
+def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deepstack=None,
+                 residual_out=None, valid_rows_only: bool = False) -> sp_problem:
+    """sp_problem from tensor shapes, strides and dtypes.  ``partials`` may be a
+    [tp, S, H] view of a larger buffer (e.g. rows [r*S, (r+1)*S) of a
+    [tp, T_pad, H] tensor) as long as each partial's rows are packed."""
+    tp, S, H = partials.shape
+    stride = _partials_stride(partials)
     return sp_problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
                       partial_dtype=_sp_dtype(partials.dtype), act_dtype=_sp_dtype(residual.dtype),
                       out_dtype=_sp_dtype(out.dtype), residual_rows=residual.shape[0],
                       deepstack_rows=0 if deepstack is None else deepstack.shape[0],
-                      residual_out=_addr(residual_out))
+                      residual_out=_addr(residual_out),
+                      partial_stride=0 if stride == S * H else stride,
+                      flags=SP_FLAG_VALID_ROWS_ONLY if valid_rows_only else 0)
+
+
+def _partials_addr(partials) -> int:
+    _partials_stride(partials)
+    return partials.data_ptr()
 
 
 def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack, out,
                           out_scale, *, tp_rank: int, num_tokens: int, residual_out=None,
-                          stream=None) -> None:
+                          valid_rows_only: bool = False, stream=None) -> None:
     """Enqueue the fused shard path (see include/sprms.h for the contract).
 
     partials [tp, S, H] f32/bf16; residual [S or tp*S, H]; weight, bias [H];
     deepstack None or [S or tp*S, H]; out [S, H] bf16/f32, or uint8 /
     float8_e4m3fn for quant modes; out_scale None, [1] f32 (static) or [S]
-    f32 (dynamic); residual_out [S, H] or None (in place).  Runs on
+    f32 (dynamic); residual_out [S, H] or None (in place).  With
+    ``valid_rows_only`` the padding rows of the outputs are left untouched
+    (out may then be a row block of an unpadded gathered tensor).  Runs on
     ``stream`` (a torch stream or raw hipStream_t int; default: torch's
     current stream on partials' device).
     """
@@ -140,12 +176,13 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
     if not partials.is_cuda:
         raise ValueError("partials must be a device tensor")
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
-                        deepstack=deepstack, residual_out=residual_out)
+                        deepstack=deepstack, residual_out=residual_out,
+                        valid_rows_only=valid_rows_only)
     with torch.cuda.device(partials.device):
         if stream is None:
             stream = torch.cuda.current_stream(partials.device)
         handle = stream if isinstance(stream, int) else stream.cuda_stream
-        _check(lib.sp_reduce_add_rmsnorm(C.byref(prob), _addr(partials), _addr(residual),
+        _check(lib.sp_reduce_add_rmsnorm(C.byref(prob), _partials_addr(partials), _addr(residual),
                                          _addr(weight), _addr(bias), float(eps), int(quant_mode),
                                          _addr(deepstack), _addr(out), _addr(out_scale), handle))
 
@@ -163,7 +200,7 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
     if stream is None:
         stream = torch.cuda.current_stream(partials.device)
     handle = stream if isinstance(stream, int) else stream.cuda_stream
-    args = (C.byref(prob), _addr(partials), _addr(residual), _addr(weight), _addr(bias),
+    args = (C.byref(prob), _partials_addr(partials), _addr(residual), _addr(weight), _addr(bias),
             float(eps), int(quant_mode), _addr(deepstack), _addr(out), _addr(out_scale), handle)
     fn = lib.sp_reduce_add_rmsnorm
 
@@ -172,6 +209,31 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
 
     launch.problem = prob  # keep the descriptor alive with the callable
     return launch
+
+
+def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int,
+                        stream=None) -> None:
+    """Gather tp shard outputs ([S, H] each, same dtype) into the unpadded
+    out [T, H] (and per-row scales [S] -> out_scale [T]); see include/sprms.h."""
+    lib = load()
+    tp = len(shards)
+    S, H = shards[0].shape
+    for t in shards:
+        if t.shape != (S, H) or t.dtype != shards[0].dtype:
+            raise ValueError("all shards must share shape and dtype")
+    if not shards[0].is_cuda:
+        raise ValueError("shards must be device tensors")
+    g = sp_gather_problem(tp=tp, dtype=_sp_dtype(shards[0].dtype), shard_rows=S, hidden=H,
+                          num_tokens=num_tokens)
+    src = (C.c_void_p * tp)(*[_addr(t) for t in shards])
+    ssrc = None
+    if shard_scales is not None:
+        ssrc = (C.c_void_p * tp)(*[_addr(t) for t in shard_scales])
+    with torch.cuda.device(shards[0].device):
+        if stream is None:
+            stream = torch.cuda.current_stream(shards[0].device)
+        handle = stream if isinstance(stream, int) else stream.cuda_stream
+        _check(lib.sp_all_gather_unpad(C.byref(g), src, ssrc, _addr(out), _addr(out_scale), handle))
 
 
 def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,

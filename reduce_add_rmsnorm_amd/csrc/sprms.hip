@@ -68,7 +68,7 @@ struct KArgs {
   const void* deepstack;  // this shard's deepstack rows or nullptr
   void* out;              // [S][H]
   float* out_scale;       // static: [1] (read); dynamic: [S] (written)
-  int64_t plane;          // S*H, distance between partials
+  int64_t plane;          // elements between partial q's row and partial q+1's row
   int32_t H;
   int32_t nvec;           // H / 8
   int32_t valid;          // rows [0, valid) are real tokens
@@ -545,6 +545,42 @@ void launch_shape(int nvec, int* vpt, int* nt) {
   *nt = n;
 }
 
+// ------------------------------------------------------------ all-gather
+
+constexpr int kMaxTp = 64;
+
+struct GArgs {
+  const char* src[kMaxTp];     // shard q's [S][H] output
+  const float* ssrc[kMaxTp];   // shard q's [S] scales (or all null)
+  char* out;                   // [T][H]
+  float* out_scale;            // [T] or null
+  int64_t S;
+  uint32_t row_bytes;          // H * element size
+  int32_t has_scale;
+};
+
+// One workgroup per gathered row t: shard q = t / S, row s = t - q*S, copied
+// unchanged with non-temporal 16-byte (or 8-byte) accesses.  The source and
+// destination descriptors cover exactly one row.
+template <int B>
+__global__ void __launch_bounds__(kMaxThreads) gather_kernel(const GArgs a) {
+  const int64_t t = blockIdx.x;
+  const int q = static_cast<int>(t / a.S);
+  const int64_t s = t - static_cast<int64_t>(q) * a.S;
+  const rsrc_t src = row_rsrc(a.src[q] + s * a.row_bytes, a.row_bytes);
+  const rsrc_t dst = row_rsrc(a.out + t * a.row_bytes, a.row_bytes);
+  for (uint32_t off = threadIdx.x * B; off < a.row_bytes; off += blockDim.x * B) {
+    if constexpr (B == 16) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, kLoadPolicy);
+      __builtin_amdgcn_raw_buffer_store_b128(v, dst, off, 0, kStorePolicy);
+    } else {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, off, 0, kLoadPolicy);
+      __builtin_amdgcn_raw_buffer_store_b64(v, dst, off, 0, kStorePolicy);
+    }
+  }
+  if (a.has_scale && threadIdx.x == 0) a.out_scale[t] = a.ssrc[q][s];
+}
+
 // ------------------------------------------------------------ host checks
 
 thread_local char g_last_error[512] = "no error";
@@ -610,6 +646,11 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
                 "quant_mode=%d unsupported (dynamic per-tensor scaling is not shard-local)", quant_mode);
   }
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SP_ERR_SHAPE, "eps must be finite and >= 0");
+  if (p->flags != 0 && p->flags != SP_FLAG_VALID_ROWS_ONLY)
+    return fail(SP_ERR_UNSUPPORTED, "flags=%d unsupported", p->flags);
+  if (p->partial_stride != 0 && p->partial_stride < S * H)
+    return fail(SP_ERR_SHAPE, "partial_stride=%lld is below S*H=%lld (partials would overlap)",
+                (long long)p->partial_stride, (long long)(S * H));
   if (S > 0) {
     if (!partials || !residual || !weight || !out)
       return fail(SP_ERR_NULL, "partials, residual, weight and out must be non-NULL");
@@ -619,6 +660,10 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   const void* dev[] = {partials, residual, weight, bias, deepstack, out, p->residual_out};
   for (const void* d : dev)
     if (d && misaligned(d)) return fail(SP_ERR_ALIGN, "device pointer %p is not 16-byte aligned", d);
+  const int64_t stride = p->partial_stride ? p->partial_stride : S * H;
+  if ((stride * static_cast<int64_t>(elt_size(p->partial_dtype))) % 16 != 0)
+    return fail(SP_ERR_ALIGN, "partial_stride=%lld elements is not a multiple of 16 bytes",
+                (long long)stride);
   if (out_scale && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
     return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", (const void*)out_scale);
 
@@ -639,24 +684,25 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
     size_t n;
   };
   const Span ins[] = {
-      {partials, static_cast<size_t>(tp * S * H) * pe},
+      {partials, static_cast<size_t>((tp - 1) * stride + S * H) * pe},
       {weight, row_a},
       {bias, bias ? row_a : 0},
       {deepstack, deepstack ? static_cast<size_t>(p->deepstack_rows) * row_a : 0},
       {residual, static_cast<size_t>(p->residual_rows) * row_a},
   };
-  const size_t out_n = static_cast<size_t>(S * H) * oe;
+  const int64_t written_rows = (p->flags & SP_FLAG_VALID_ROWS_ONLY) ? plan->valid : S;
+  const size_t out_n = static_cast<size_t>(written_rows * H) * oe;
   for (const Span& in : ins)
     if (overlap(out, out_n, in.p, in.n)) return fail(SP_ERR_SHAPE, "out overlaps an input");
   if (p->residual_out && p->residual_out != res_used) {
-    const size_t ro_n = static_cast<size_t>(S) * row_a;
+    const size_t ro_n = static_cast<size_t>(written_rows) * row_a;
     for (const Span& in : ins)
       if (overlap(p->residual_out, ro_n, in.p, in.n))
         return fail(SP_ERR_SHAPE, "residual_out overlaps an input (pass NULL for in-place)");
     if (overlap(p->residual_out, ro_n, out, out_n)) return fail(SP_ERR_SHAPE, "residual_out overlaps out");
   }
   if (quant_mode == SP_QUANT_DYNAMIC_TOKEN && out_scale) {
-    const size_t sn = static_cast<size_t>(S) * 4;
+    const size_t sn = static_cast<size_t>(written_rows) * 4;
     for (const Span& in : ins)
       if (overlap(out_scale, sn, in.p, in.n)) return fail(SP_ERR_SHAPE, "out_scale overlaps an input");
     if (overlap(out_scale, sn, out, out_n)) return fail(SP_ERR_SHAPE, "out_scale overlaps out");
@@ -683,7 +729,9 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   Plan plan;
   int rc = check(p, partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, &plan);
   if (rc != SP_OK) return rc;
-  if (p->shard_rows == 0) return SP_OK;
+  // rows to launch: all S rows, or only the valid ones (padding rows untouched)
+  const int64_t launch_rows = (p->flags & SP_FLAG_VALID_ROWS_ONLY) ? plan.valid : p->shard_rows;
+  if (launch_rows == 0) return SP_OK;
 
   const int64_t H = p->hidden;
   const size_t ae = elt_size(p->act_dtype);
@@ -696,7 +744,7 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   ka.deepstack = deepstack ? static_cast<const char*>(deepstack) + plan.doff * H * ae : nullptr;
   ka.out = out;
   ka.out_scale = out_scale;
-  ka.plane = p->shard_rows * H;
+  ka.plane = p->partial_stride ? p->partial_stride : p->shard_rows * H;
   ka.H = static_cast<int32_t>(H);
   ka.nvec = static_cast<int32_t>(H / kVec);
   ka.valid = static_cast<int32_t>(plan.valid);
@@ -714,10 +762,71 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   KFn fn = pick_kernel(p->partial_dtype, p->act_dtype, om, p->tp, vpt);
   if (!fn) return fail(SP_ERR_UNSUPPORTED, "no kernel for this dtype / mode combination");
   void* args[] = {&ka};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(p->shard_rows)),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(launch_rows)),
                                  dim3(static_cast<unsigned>(nt)), args, 0,
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SP_OK;
+}
+
+int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
+                        const float* const* shard_scales, void* out, float* out_scale,
+                        void* stream) {
+  if (!g) return fail(SP_ERR_NULL, "gather descriptor is NULL");
+  if (g->tp < 1 || g->tp > kMaxTp) return fail(SP_ERR_SHAPE, "tp=%d outside [1, %d]", g->tp, kMaxTp);
+  const int64_t S = g->shard_rows, H = g->hidden, T = g->num_tokens;
+  if (S < 0 || S > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld outside [0, 2^31)", (long long)S);
+  if (H < 8 || H > kMaxHidden || H % 8 != 0)
+    return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, %d]", (long long)H, kMaxHidden);
+  if (T < 0 || T > g->tp * S || T > INT32_MAX)
+    return fail(SP_ERR_SHAPE, "num_tokens=%lld outside [0, tp*S=%lld]", (long long)T, (long long)(g->tp * S));
+  const size_t e = elt_size(g->dtype);
+  if (e == 0) return fail(SP_ERR_DTYPE, "dtype=%d unknown", g->dtype);
+  if (T == 0) return SP_OK;
+  if (!shards || !out) return fail(SP_ERR_NULL, "shards and out must be non-NULL");
+  if ((shard_scales == nullptr) != (out_scale == nullptr))
+    return fail(SP_ERR_NULL, "shard_scales and out_scale must both be given or both be NULL");
+  const size_t row_bytes = static_cast<size_t>(H) * e;
+  // 16-byte accesses when rows are a multiple of 16 bytes, else 8-byte ones;
+  // every row start must be aligned to the access width
+  const int B = row_bytes % 16 == 0 ? 16 : 8;
+  const uintptr_t amask = static_cast<uintptr_t>(B - 1);
+  if (reinterpret_cast<uintptr_t>(out) & amask)
+    return fail(SP_ERR_ALIGN, "out %p is not %d-byte aligned", out, B);
+  if (out_scale && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
+    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", (void*)out_scale);
+  const size_t out_n = static_cast<size_t>(T) * row_bytes;
+  GArgs ga;
+  memset(&ga, 0, sizeof ga);
+  for (int q = 0; q < g->tp; ++q) {
+    if (!shards[q]) return fail(SP_ERR_NULL, "shards[%d] is NULL", q);
+    if (reinterpret_cast<uintptr_t>(shards[q]) & amask)
+      return fail(SP_ERR_ALIGN, "shards[%d] %p is not %d-byte aligned", q, shards[q], B);
+    if (overlap(out, out_n, shards[q], static_cast<size_t>(S) * row_bytes))
+      return fail(SP_ERR_SHAPE, "out overlaps shards[%d]", q);
+    ga.src[q] = static_cast<const char*>(shards[q]);
+    if (shard_scales) {
+      if (!shard_scales[q]) return fail(SP_ERR_NULL, "shard_scales[%d] is NULL", q);
+      if (reinterpret_cast<uintptr_t>(shard_scales[q]) & 3u)
+        return fail(SP_ERR_ALIGN, "shard_scales[%d] is not 4-byte aligned", q);
+      if (overlap(out_scale, static_cast<size_t>(T) * 4, shard_scales[q], static_cast<size_t>(S) * 4))
+        return fail(SP_ERR_SHAPE, "out_scale overlaps shard_scales[%d]", q);
+      ga.ssrc[q] = shard_scales[q];
+    }
+  }
+  ga.out = static_cast<char*>(out);
+  ga.out_scale = out_scale;
+  ga.S = S;
+  ga.row_bytes = static_cast<uint32_t>(row_bytes);
+  ga.has_scale = shard_scales != nullptr;
+  int nt = static_cast<int>((row_bytes / B + 63) / 64 * 64);
+  nt = nt > kMaxThreads ? kMaxThreads : nt;
+  void* args[] = {&ga};
+  const void* fn = B == 16 ? reinterpret_cast<const void*>(&gather_kernel<16>)
+                           : reinterpret_cast<const void*>(&gather_kernel<8>);
+  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(T)), dim3(static_cast<unsigned>(nt)), args,
+                                   0, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SP_ERR_HIP, "gather launch failed: %s", hipGetErrorString(err));
   return SP_OK;
 }
 

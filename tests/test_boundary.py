@@ -131,11 +131,57 @@ def test_valid_problems_pass():
     (dict(a=dict(out=BASE + 4096)), sp.SP_ERR_SHAPE),                     # out overlaps partials
     (dict(p=dict(residual_out=BASE + 2 * GB)), sp.SP_ERR_SHAPE),          # residual_out on weight
     (dict(p=dict(residual_out=BASE + 3 * GB)), sp.SP_ERR_SHAPE),          # residual_out on out
+    (dict(p=dict(partial_stride=128 * 4096 - 8)), sp.SP_ERR_SHAPE),       # partials would overlap
+    (dict(p=dict(partial_stride=128 * 4096 + 4)), sp.SP_ERR_ALIGN),       # 8-byte plane step
+    (dict(p=dict(flags=2)), sp.SP_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems_are_rejected(case, expect):
     status, msg = validate(problem(**case.get("p", {})), **case.get("a", {}))
     assert status == expect, msg
     assert msg and msg != "no error"
+
+
+def test_strided_and_valid_rows_only_problems_pass():
+    assert validate(problem(partial_stride=1024 * 4096))[0] == sp.SP_OK
+    assert validate(problem(flags=sp.SP_FLAG_VALID_ROWS_ONLY))[0] == sp.SP_OK
+    # with valid rows only, out may end right where the 104 valid rows end
+    status, msg = validate(problem(flags=sp.SP_FLAG_VALID_ROWS_ONLY), out=BASE - 104 * 4096 * 2)
+    assert status == sp.SP_OK, msg
+    assert validate(problem(), out=BASE - 104 * 4096 * 2)[0] == sp.SP_ERR_SHAPE
+
+
+def _gather(tp=2, S=4, H=16, T=8, dtype=sp.SP_BF16, shards=None, scales=None, out=BASE + 8 * GB,
+            out_scale=None):
+    import ctypes as C
+    lib = sp.load()
+    g = sp.sp_gather_problem(tp=tp, dtype=dtype, shard_rows=S, hidden=H, num_tokens=T)
+    shards = shards if shards is not None else [BASE + q * GB for q in range(tp)]
+    src = (C.c_void_p * len(shards))(*shards)
+    ssrc = None if scales is None else (C.c_void_p * len(scales))(*scales)
+    return lib.sp_all_gather_unpad(C.byref(g), src, ssrc, out, out_scale, None), sp.sp_last_error()
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(tp=0), sp.SP_ERR_SHAPE),
+    (dict(tp=65, shards=[BASE] * 65), sp.SP_ERR_SHAPE),
+    (dict(T=9), sp.SP_ERR_SHAPE),
+    (dict(H=12), sp.SP_ERR_SHAPE),
+    (dict(dtype=9), sp.SP_ERR_DTYPE),
+    (dict(shards=[BASE, 0]), sp.SP_ERR_NULL),
+    (dict(shards=[BASE, BASE + GB + 8]), sp.SP_ERR_ALIGN),
+    (dict(out=BASE + 8 * GB + 4), sp.SP_ERR_ALIGN),
+    (dict(out=BASE + 64), sp.SP_ERR_SHAPE),                        # out overlaps shard 0
+    (dict(scales=[BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_NULL),  # no out_scale
+    (dict(out_scale=BASE + 6 * GB), sp.SP_ERR_NULL),                # no shard scales
+])
+def test_gather_rejects_invalid_problems(case, expect):
+    status, msg = _gather(**case)
+    assert status == expect, msg
+
+
+def test_gather_empty_is_a_no_op():
+    assert _gather(T=0)[0] == sp.SP_OK
+    assert _gather(S=0, T=0)[0] == sp.SP_OK
 
 
 def test_null_descriptor():
@@ -149,3 +195,18 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         sp.sp_reduce_add_rmsnorm(x, x[0], x[0, 0], None, 1e-6, 0, None, x[0], None, tp_rank=0,
                                  num_tokens=8)
+
+
+def test_plain_c_client_compiles_links_and_runs(tmp_path):
+    """A C program that includes only include/sprms.h builds with gcc, links
+    against libsprms.so and gets the documented answers from the host-only
+    entry points."""
+    sp.load()
+    exe = tmp_path / "c_abi_check"
+    lib_dir = os.path.dirname(sp.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), "-L", lib_dir,
+                    "-lsprms", f"-Wl,-rpath,{lib_dir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert "c abi ok" in out.stdout

@@ -35,6 +35,10 @@ MUTATIONS = {
     "weight_ignored": ("y[h] = z[h] * rstd * load(weight, p->act_dtype, h);",
                        "y[h] = z[h] * rstd;"),
     "static_scale_multiplied": ("y[h] / (double)static_scale)", "y[h] * (double)static_scale)"),
+    "gather_rows_reversed": ("(const char*)shards[q] + (size_t)s * row, row);",
+                             "(const char*)shards[q] + (size_t)(S - 1 - s) * row, row);"),
+    "gather_scale_from_wrong_rank": ("if (scales) out_scale[t] = scales[q][s];",
+                                     "if (scales) out_scale[t] = scales[0][s];"),
 }
 
 

@@ -239,6 +239,14 @@ def test_reduce_scatter_plus_all_gather_equals_all_reduce(quant):
         cat = np.concatenate([x[key] for x in B])
         np.testing.assert_array_equal(cat[:T], A[key][:T], err_msg=key)
         assert not np.any(cat[T:]), key  # padding rows of the last rank are zero
+    # the same through the oracle's AllGather + unpad ([SP/FC] §3.3)
+    for key in ("residual_out", "out"):
+        g, _ = oracle.all_gather_unpad([x[key] for x in B], num_tokens=T)
+        np.testing.assert_array_equal(g, A[key][:T], err_msg=key)
+    if quant == DYNAMIC:
+        g, gs = oracle.all_gather_unpad([x["out"] for x in B], [x["out_scale"] for x in B],
+                                        num_tokens=T)
+        np.testing.assert_array_equal(gs, A["out_scale"][:T])
 
 
 def test_shard_residual_equals_replicated_chunk():
@@ -425,3 +433,29 @@ def test_bf16_inputs_are_decoded_exactly():
     np.testing.assert_array_equal(bf16_bits_to_f64(bits),
                                   [oracle.bf16_to_double(int(b)) for b in bits])
     assert oracle.bf16_to_double(0x3F80) == 1.0 and oracle.bf16_to_double(0xC000) == -2.0
+
+
+def test_all_gather_unpad_worked_example():
+    # [PR18671] §2: 3500 tokens padded to 3504 over TP=16, 219 per rank; the
+    # gathered, unpadded tensor has 3500 rows, rank 15 contributes its first
+    # 215 rows starting at row 3285, and its 4 padding rows are dropped.
+    with open(os.path.join(GOLDEN, "shard_geometry.json")) as f:
+        g = json.load(f)
+    c = g["cases"][-1]
+    tp, S, T = c["tp"], c["shard_rows"], c["num_tokens"]
+    H = 8
+    shards = [np.empty((S, H), np.uint16) for _ in range(tp)]
+    for q in range(tp):
+        shards[q][:, 0] = q
+        shards[q][:, 1] = np.arange(S)
+        shards[q][:, 2:] = 7
+    scales = [np.full(S, q, np.float32) + np.arange(S, dtype=np.float32) / 1000 for q in range(tp)]
+    out, out_scale = oracle.all_gather_unpad(shards, scales, num_tokens=T)
+    assert out.shape == (T, H)
+    start, valid = c["local_start"], c["valid_rows"]
+    np.testing.assert_array_equal(out[start:, 0], tp - 1)
+    np.testing.assert_array_equal(out[start:, 1], np.arange(valid))
+    assert out[start - 1, 0] == tp - 2 and out[start - 1, 1] == S - 1
+    np.testing.assert_array_equal(out[:S, 1], np.arange(S))
+    np.testing.assert_array_equal(out_scale[start:], scales[-1][:valid])
+    assert T - start == valid and S - valid == g["pad_rows_total"]

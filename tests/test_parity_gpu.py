@@ -314,3 +314,66 @@ def test_bf16_conversion_sweep_exact(dev):
         got = _conversion_call(dev, chunk, QUANT_NONE)
         want = oracle.bf16_from_double_array(chunk.astype(np.float64))
         np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------------ graph capture
+
+
+def _bits(t):
+    return t.view(torch.uint8).clone()
+
+
+@pytest.mark.parametrize("name", ["C5", "C4"])
+def test_hip_graph_capture_replays_match_eager(dev, name):
+    """The call records one kernel node (no memset, no allocation); replays with
+    eager work and synchronisations between them must reproduce the eager
+    outputs bit for bit; the static scale is read on the device at replay time."""
+    base = WORKLOADS[name]
+    w = dataclasses.replace(base, num_tokens=base.tp * 64, num_tokens_pad=base.tp * 64)
+    say(f"graph capture {name}: S=64 H={w.hidden}")
+    x = make_inputs(w, rank=w.rank, device=dev, shard_rows=64)
+    S, H = 64, w.hidden
+    scale = (torch.tensor([0.02], dtype=torch.float32, device=dev) if w.quant_mode == QUANT_STATIC_TENSOR
+             else torch.empty((S,), dtype=torch.float32, device=dev))
+    out = torch.empty((S, H), dtype=w.out_dtype, device=dev)
+    res = torch.empty((S, H), dtype=w.act_dtype, device=dev)
+
+    def call():
+        sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], w.eps,
+                                 w.quant_mode, x["deepstack"], out, scale, tp_rank=w.rank,
+                                 num_tokens=w.num_tokens, residual_out=res)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [_bits(out), _bits(res), _bits(scale)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for it in range(4):
+        out.view(torch.uint8).fill_(0x5A)
+        res.view(torch.uint8).fill_(0x5A)
+        if w.quant_mode == QUANT_DYNAMIC_TOKEN:
+            scale.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [_bits(out), _bits(res), _bits(scale)]
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {it} differs from the eager call"
+    if w.quant_mode == QUANT_STATIC_TENSOR:
+        scale.fill_(0.04)  # read on the device at replay time
+        g.replay()
+        torch.cuda.synchronize()
+        call_out = out.clone()
+        scale.fill_(0.04)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(call_out.view(torch.uint8), out.view(torch.uint8))
+        assert not torch.equal(call_out.view(torch.uint8), ref[0])
