@@ -13,6 +13,7 @@ bounded sample of the same shard.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -28,14 +29,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import reduce_add_rmsnorm_amd as sp  # noqa: E402
-from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_STATIC_TENSOR,  # noqa: E402
-                                           WORKLOADS, make_inputs)
+from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK,  # noqa: E402
+                                           QUANT_STATIC_TENSOR, WORKLOADS, make_inputs)
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + shard tokens/s for fused reduce-add-RMSNorm"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 KERNEL_SRC = os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc", "sprms.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
-QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3"}
+QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3",
+               4: "block-scaled (32-element E8M0 scales)"}
 
 
 def kernel_hash() -> str:
@@ -66,16 +68,18 @@ def static_scale() -> float:
 def setup(w, dev):
     x = make_inputs(w, rank=w.rank, device=dev)
     S, H = w.shard_rows, w.hidden
-    out = torch.empty((S, H), dtype=w.out_dtype, device=dev)
+    out = torch.empty((S, H // 2 if w.fp4 else H), dtype=w.out_dtype, device=dev)
     res_out = torch.empty((S, H), dtype=w.act_dtype, device=dev)
     scale = None
     if w.quant_mode == QUANT_STATIC_TENSOR:
         scale = torch.tensor([static_scale()], dtype=torch.float32, device=dev)
     elif w.quant_mode == QUANT_DYNAMIC_TOKEN:
         scale = torch.empty((S,), dtype=torch.float32, device=dev)
+    elif w.quant_mode == QUANT_MX_BLOCK:
+        scale = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)
     launch = sp.prepare(x["partials"], x["residual"], x["weight"], x["bias"], w.eps, w.quant_mode,
                         x["deepstack"], out, scale, tp_rank=w.rank, num_tokens=w.num_tokens,
-                        residual_out=res_out)
+                        residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if w.fp4 else None)
     return x, launch, (out, res_out, scale)
 
 
@@ -128,7 +132,7 @@ def cpu_baseline(w, x, budget_s: float):
         t0 = time.perf_counter()
         oracle.reduce_add_rmsnorm(P, R, wt, b, w.eps, w.quant_mode, D, tp_rank=r,
                                   num_tokens=w.tp * n,
-                                  out_dtype=oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
+                                  out_dtype=oracle.ORC_E2M1 if w.fp4 else oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
                                   else oracle.ORC_E4M3,
                                   static_scale=static_scale() if w.quant_mode == QUANT_STATIC_TENSOR
                                   else 1.0, want_debug=False)
@@ -179,6 +183,9 @@ def main():
     ap.add_argument("--path", default="fused", choices=["fused", "gather"],
                     help="fused: the shard kernel (the headline); gather: AllGather + unpad of "
                          "every rank's shard output of the workload into [T, H] on this GPU")
+    ap.add_argument("--quant", default=None, choices=["mxfp8", "mxfp4"],
+                    help="replace the workload's output quantisation by block scaling "
+                         "(32-element E8M0 scales) with e4m3 or e2m1 elements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling hardware byte counters)")
@@ -194,6 +201,9 @@ def main():
         copy_calibration(args, dev)
         return
     w = WORKLOADS[args.workload]
+    if args.quant:
+        w = dataclasses.replace(w, quant_mode=QUANT_MX_BLOCK, out_dtype=torch.uint8,
+                                fp4=args.quant == "mxfp4")
     sp.load()
     if args.path == "gather":
         x, launch, nbytes, tokens = setup_gather(w, dev)
@@ -236,7 +246,8 @@ def main():
     ms_per_step = wall * 1000.0 / args.steps
     value = nbytes / (ms_per_step / 1000.0) / 1e9
     achieved = nbytes / (avg_ms / 1000.0) / 1e9
-    traffic = measured_traffic(w.name if args.path == "fused" else f"{w.name}-gather")
+    traffic = measured_traffic(w.name if args.path == "fused" and not args.quant else
+                               f"{w.name}-{args.path}-{args.quant}")
 
     result = {
         "metric": METRIC,
@@ -258,7 +269,9 @@ def main():
             "path": "sp_reduce_add_rmsnorm" if args.path == "fused" else "sp_all_gather_unpad",
             "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
             "shard_rows": w.shard_rows, "hidden": w.hidden,
-            "quant": QUANT_NAMES[w.quant_mode], "deepstack": w.deepstack, "bias": w.bias,
+            "quant": QUANT_NAMES[w.quant_mode] + (
+                (" e2m1" if w.fp4 else " e4m3") if w.quant_mode == QUANT_MX_BLOCK else ""),
+            "deepstack": w.deepstack, "bias": w.bias,
             "algorithmic_bytes": nbytes,
         },
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

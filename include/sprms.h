@@ -38,8 +38,9 @@
 extern "C" {
 #endif
 
-/* Storage types. */
-typedef enum { SP_F32 = 0, SP_BF16 = 1, SP_FP8_E4M3 = 2 } sp_dtype;
+/* Storage types.  SP_FP4_E2M1 packs two elements per byte, the even
+ * element in the low nibble. */
+typedef enum { SP_F32 = 0, SP_BF16 = 1, SP_FP8_E4M3 = 2, SP_FP4_E2M1 = 3 } sp_dtype;
 
 /* Output quantisation.  Static per-tensor and dynamic per-token scales are
  * computable on one shard; dynamic per-tensor is not (its max spans every
@@ -48,7 +49,15 @@ typedef enum { SP_F32 = 0, SP_BF16 = 1, SP_FP8_E4M3 = 2 } sp_dtype;
 typedef enum {
   SP_QUANT_NONE = 0,           /* out = y in out_dtype (SP_BF16 or SP_F32) */
   SP_QUANT_STATIC_TENSOR = 1,  /* out = e4m3(y / out_scale[0]), out_scale read */
-  SP_QUANT_DYNAMIC_TOKEN = 2   /* out_scale[s] = max_h|y| / 448, out = e4m3(y / out_scale[s]) */
+  SP_QUANT_DYNAMIC_TOKEN = 2,  /* out_scale[s] = max_h|y| / 448, out = e4m3(y / out_scale[s]) */
+  /* 3 is reserved for dynamic per-tensor scaling and always rejected */
+  SP_QUANT_MX_BLOCK = 4        /* per-block scaling, blocks of 32 consecutive elements of a row
+                                  (the per-block row of the quantisation table above), in the
+                                  OCP microscaling form native to gfx950: per block
+                                  e = floor(log2 max|y|) - emax (emax 8 for e4m3, 2 for e2m1),
+                                  clamped to [-127, 127] (an all-zero block gets -127);
+                                  out = elem(clamp(y * 2^-e)) in out_dtype SP_FP8_E4M3 (MXFP8)
+                                  or SP_FP4_E2M1 (MXFP4); out_scale[s][b] = e + 127 (E8M0) */
 } sp_quant;
 
 typedef enum {
@@ -70,7 +79,8 @@ typedef struct {
   int64_t num_tokens;     /* valid tokens T over all ranks, 0 <= T <= tp * S */
   int32_t partial_dtype;  /* SP_F32 | SP_BF16 */
   int32_t act_dtype;      /* residual, deepstack, weight, bias, residual_out: SP_F32 | SP_BF16 */
-  int32_t out_dtype;      /* SP_BF16 | SP_F32 with SP_QUANT_NONE; SP_FP8_E4M3 with a quant mode */
+  int32_t out_dtype;      /* SP_BF16 | SP_F32 with SP_QUANT_NONE; SP_FP8_E4M3 with the static or
+                             per-token modes; SP_FP8_E4M3 | SP_FP4_E2M1 with SP_QUANT_MX_BLOCK */
   int64_t residual_rows;  /* S (shard residual) or tp*S (replicated: block tp_rank is used) */
   int64_t deepstack_rows; /* 0 iff deepstack == NULL, else S or tp*S (block tp_rank is used) */
   void* residual_out;     /* device [S][H] act_dtype, or NULL: write the used residual rows in place */
@@ -108,9 +118,12 @@ typedef struct {
  *   eps        >= 0, added to the mean of squares inside the square root
  *   quant_mode sp_quant
  *   deepstack  [deepstack_rows][H] act_dtype, or NULL
- *   out        [S][H] out_dtype (e4m3 codes are one byte each)
+ *   out        [S][H] out_dtype (e4m3 codes are one byte each; e2m1 codes two per byte,
+ *              i.e. [S][H/2] bytes)
  *   out_scale  SP_QUANT_STATIC_TENSOR: [1] f32 scale, read on the device (> 0);
- *              SP_QUANT_DYNAMIC_TOKEN: [S] f32, written; SP_QUANT_NONE: ignored
+ *              SP_QUANT_DYNAMIC_TOKEN: [S] f32, written;
+ *              SP_QUANT_MX_BLOCK: [S][H/32] E8M0 bytes, written (H % 32 == 0);
+ *              SP_QUANT_NONE: ignored
  *   stream     hipStream_t to enqueue on (NULL = default stream)
  *
  * Arithmetic: fp32 throughout; partial sums in ascending rank order, then
@@ -127,15 +140,17 @@ typedef struct {
  */
 int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
                           const void* weight, const void* bias, float eps, int quant_mode,
-                          const void* deepstack, void* out, float* out_scale, void* stream);
+                          const void* deepstack, void* out, void* out_scale, void* stream);
 
 /* Problem descriptor of sp_all_gather_unpad (host memory, read during the call only). */
 typedef struct {
-  int32_t tp;          /* number of shards, 1 <= tp <= 64 */
-  int32_t dtype;       /* element type of the shard outputs: SP_F32 | SP_BF16 | SP_FP8_E4M3 */
-  int64_t shard_rows;  /* S, rows per shard (padded), 0 <= S <= 2^31 - 1 */
-  int64_t hidden;      /* H, H % 8 == 0, 8 <= H <= 32768 */
-  int64_t num_tokens;  /* T, valid tokens over all shards, 0 <= T <= tp * S, T < 2^31 */
+  int32_t tp;               /* number of shards, 1 <= tp <= 64 */
+  int32_t dtype;            /* element type of the shard outputs (any sp_dtype) */
+  int64_t shard_rows;       /* S, rows per shard (padded), 0 <= S <= 2^31 - 1 */
+  int64_t hidden;           /* H, H % 8 == 0 (H % 16 for e2m1), 8 <= H <= 32768 */
+  int64_t num_tokens;       /* T, valid tokens over all shards, 0 <= T <= tp * S, T < 2^31 */
+  int64_t scale_row_bytes;  /* bytes of scale per row, 0 <= . <= 65536: 0 (none), 4 (one f32
+                               per token), H/32 (one E8M0 byte per 32-element block) */
 } sp_gather_problem;
 
 /*
@@ -150,10 +165,11 @@ typedef struct {
  *   shards        host array of tp device pointers, shard q's output [S][H] (dtype).
  *                 On one GPU these are local buffers; on a node they may be
  *                 peer-mapped buffers of the other ranks (the kernel pulls).
- *   shard_scales  host array of tp device pointers to [S] f32 per-row scales, or NULL
+ *   shard_scales  host array of tp device pointers to [S][scale_row_bytes] scales, or
+ *                 NULL (then scale_row_bytes must be 0)
  *   out           device [T][H] dtype; out and every shard 16-byte aligned when a
  *                 row is a multiple of 16 bytes, else 8-byte aligned
- *   out_scale     device [T] f32; required iff shard_scales != NULL
+ *   out_scale     device [T][scale_row_bytes]; required iff shard_scales != NULL
  *   stream        hipStream_t (NULL = default stream)
  *
  * Bytes are copied unchanged (bit-exact).  Same error convention as
@@ -161,7 +177,7 @@ typedef struct {
  * out must not overlap a shard.  T == 0 enqueues nothing.
  */
 int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
-                        const float* const* shard_scales, void* out, float* out_scale,
+                        const void* const* shard_scales, void* out, void* out_scale,
                         void* stream);
 
 /*
@@ -172,7 +188,7 @@ int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
  */
 int sp_validate(const sp_problem* p, const void* partials, const void* residual,
                 const void* weight, const void* bias, float eps, int quant_mode,
-                const void* deepstack, const void* out, const float* out_scale);
+                const void* deepstack, const void* out, const void* out_scale);
 
 /*
  * sp_shard_geometry -- contiguous shard layout (vllm-ascend PR #18671

@@ -7,9 +7,11 @@ only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 from .oracle import (  # noqa: F401
     ORC_BF16,
+    ORC_E2M1,
     ORC_E4M3,
     ORC_F32,
     QUANT_DYNAMIC_TOKEN,
+    QUANT_MX_BLOCK,
     QUANT_NONE,
     QUANT_STATIC_TENSOR,
     OracleError,
@@ -18,6 +20,9 @@ from .oracle import (  # noqa: F401
     bf16_from_double_array,
     bf16_to_double,
     build,
+    e2m1_from_double,
+    e2m1_from_double_array,
+    e2m1_to_double,
     e4m3_from_double,
     e4m3_from_double_array,
     e4m3_to_double,

@@ -14,8 +14,8 @@ import subprocess
 
 import numpy as np
 
-ORC_F32, ORC_BF16, ORC_E4M3 = 0, 1, 2
-QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN = 0, 1, 2
+ORC_F32, ORC_BF16, ORC_E4M3, ORC_E2M1 = 0, 1, 2, 3
+QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK = 0, 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sprms_oracle.c")
@@ -79,9 +79,15 @@ def _load():
     lib.orc_e4m3_from_double.restype = C.c_uint8
     lib.orc_e4m3_to_double.argtypes = [C.c_uint8]
     lib.orc_e4m3_to_double.restype = C.c_double
-    lib.orc_all_gather_unpad.argtypes = [i32, i64, i64, i64, i32, C.POINTER(vp), C.POINTER(vp),
+    lib.orc_all_gather_unpad.argtypes = [i32, i64, i64, i64, C.POINTER(vp), i64, C.POINTER(vp),
                                          vp, vp]
     lib.orc_all_gather_unpad.restype = C.c_int
+    lib.orc_e2m1_from_double.argtypes = [C.c_double]
+    lib.orc_e2m1_from_double.restype = C.c_uint8
+    lib.orc_e2m1_to_double.argtypes = [C.c_uint8]
+    lib.orc_e2m1_to_double.restype = C.c_double
+    lib.orc_e2m1_from_double_n.argtypes = [vp, i64, vp]
+    lib.orc_e2m1_from_double_n.restype = None
     lib.orc_bf16_from_double_n.argtypes = [vp, i64, vp]
     lib.orc_bf16_from_double_n.restype = None
     lib.orc_e4m3_from_double_n.argtypes = [vp, i64, vp]
@@ -135,7 +141,7 @@ def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepst
     for name, a in (("weight", weight), ("bias", bias), ("deepstack", deepstack)):
         if a is not None and _dtype_code(a) != act:
             raise OracleError(f"{name} dtype differs from the residual dtype")
-    if quant_mode != QUANT_NONE:
+    if quant_mode != QUANT_NONE and not (quant_mode == QUANT_MX_BLOCK and out_dtype == ORC_E2M1):
         out_dtype = ORC_E4M3
     prob = _Problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
                     partial_dtype=_dtype_code(partials), act_dtype=act, out_dtype=out_dtype,
@@ -148,9 +154,12 @@ def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepst
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         n = rows_arr.shape[0]
     res_out = np.zeros((n, H), dtype=residual.dtype)
-    out_np = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_E4M3: np.uint8}[out_dtype]
-    out = np.zeros((n, H), dtype=out_np)
-    scale = np.zeros((n,), dtype=np.float32)
+    out_np = {ORC_F32: np.float32, ORC_BF16: np.uint16, ORC_E4M3: np.uint8, ORC_E2M1: np.uint8}
+    out = np.zeros((n, H // 2 if out_dtype == ORC_E2M1 else H), dtype=out_np[out_dtype])
+    if quant_mode == QUANT_MX_BLOCK:
+        scale = np.zeros((n, H // 32), dtype=np.uint8)
+    else:
+        scale = np.zeros((n,), dtype=np.float32)
     z = np.zeros((n, H), dtype=np.float64) if want_debug else None
     y = np.zeros((n, H), dtype=np.float64) if want_debug else None
     rc = lib.orc_reduce_add_rmsnorm(C.byref(prob), _ptr(partials), _ptr(residual), _ptr(weight),
@@ -160,7 +169,7 @@ def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepst
     if rc != 0:
         raise OracleError(f"orc_reduce_add_rmsnorm failed: {rc}")
     result = {"residual_out": res_out, "out": out, "z": z, "y": y}
-    if quant_mode == QUANT_DYNAMIC_TOKEN:
+    if quant_mode in (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK):
         result["out_scale"] = scale
     return result
 
@@ -198,21 +207,39 @@ def e4m3_from_double_array(x) -> np.ndarray:
 
 
 def all_gather_unpad(shards, scales=None, *, num_tokens):
-    """Gather tp host shard outputs [S, H] (any 1/2/4-byte dtype) into [T, H];
-    per-row scales [S] into [T].  Returns (out, out_scale or None)."""
+    """Gather tp host shard outputs [S, ...] (rows of any byte width) into
+    [T, ...]; per-row scales [S, ...] likewise.  Returns (out, out_scale or None)."""
     lib = _load()
     shards = [np.ascontiguousarray(a) for a in shards]
     tp = len(shards)
-    S, H = shards[0].shape
-    e = shards[0].dtype.itemsize
-    out = np.zeros((num_tokens, H), dtype=shards[0].dtype)
+    S = shards[0].shape[0]
+    row_bytes = shards[0].nbytes // max(S, 1)
+    out = np.zeros((num_tokens,) + shards[0].shape[1:], dtype=shards[0].dtype)
     src = (C.c_void_p * tp)(*[a.ctypes.data for a in shards])
-    ssrc, out_scale = None, None
+    ssrc, out_scale, srow = None, None, 0
     if scales is not None:
-        scales = [np.ascontiguousarray(a, dtype=np.float32) for a in scales]
+        scales = [np.ascontiguousarray(a) for a in scales]
         ssrc = (C.c_void_p * tp)(*[a.ctypes.data for a in scales])
-        out_scale = np.zeros((num_tokens,), dtype=np.float32)
-    rc = lib.orc_all_gather_unpad(tp, S, H, num_tokens, e, src, ssrc, _ptr(out), _ptr(out_scale))
+        srow = scales[0].nbytes // max(S, 1)
+        out_scale = np.zeros((num_tokens,) + scales[0].shape[1:], dtype=scales[0].dtype)
+    rc = lib.orc_all_gather_unpad(tp, S, row_bytes, num_tokens, src, srow, ssrc, _ptr(out),
+                                  _ptr(out_scale))
     if rc != 0:
         raise OracleError(f"orc_all_gather_unpad failed: {rc}")
     return out, out_scale
+
+
+def e2m1_from_double(x: float) -> int:
+    return int(_load().orc_e2m1_from_double(float(x)))
+
+
+def e2m1_to_double(code: int) -> float:
+    return float(_load().orc_e2m1_to_double(int(code)))
+
+
+def e2m1_from_double_array(x) -> np.ndarray:
+    """Element-wise orc_e2m1_from_double over a float64 array (one code per uint8)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_e2m1_from_double_n(_ptr(x), x.size, _ptr(out))
+    return out

@@ -117,6 +117,35 @@ uint8_t orc_e4m3_from_double(double x) {
   return (uint8_t)(best | (signbit(x) ? 0x80 : 0x00));
 }
 
+/* OCP FP4 E2M1: sign, 2 exponent bits with bias 1, 1 mantissa bit.  Exponent
+ * field 0 holds the subnormal m/2; no NaN, no infinity: magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6. */
+double orc_e2m1_to_double(uint8_t code) {
+  int s = (code >> 3) & 1;
+  int e = (code >> 1) & 3;
+  int m = code & 1;
+  double v = e == 0 ? (double)m / 2.0 : ldexp(1.0 + (double)m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
+/* Clamp to [-6, 6], then the nearest of the 8 magnitudes by exhaustive search,
+ * ties to the even mantissa; the sign bit follows the sign of x. */
+uint8_t orc_e2m1_from_double(double x) {
+  if (isnan(x)) return 0x7; /* no NaN code: saturate (never produced by the path) */
+  double a = fabs(x);
+  if (a > 6.0) a = 6.0;
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 7; ++c) {
+    double err = fabs(orc_e2m1_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (signbit(x) ? 0x8 : 0x0));
+}
+
 /* --------------------------------------------------------------- elements */
 
 static size_t elt_size(int32_t dt) {
@@ -124,7 +153,7 @@ static size_t elt_size(int32_t dt) {
     case ORC_F32: return 4;
     case ORC_BF16: return 2;
     case ORC_E4M3: return 1;
-    default: return 0;
+    default: return 0;  /* ORC_E2M1 rows are H/2 bytes: see row_bytes() */
   }
 }
 
@@ -153,6 +182,10 @@ static void store(void* base, int32_t dt, int64_t idx, double v) {
   }
 }
 
+static size_t row_bytes(int32_t dt, int64_t H) {
+  return dt == ORC_E2M1 ? (size_t)H / 2 : (size_t)H * elt_size(dt);
+}
+
 /* -------------------------------------------------------------- geometry */
 
 int orc_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp,
@@ -178,7 +211,7 @@ int orc_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp,
 static int validate(const orc_problem* p, const void* partials, const void* residual,
                     const void* weight, int32_t quant_mode, const void* deepstack,
                     float static_scale, int64_t n_rows, const int64_t* rows,
-                    const void* residual_out, const void* out, const float* out_scale) {
+                    const void* residual_out, const void* out, const void* out_scale) {
   if (!p) return ORC_ERR_NULL;
   if (p->tp < 1 || p->tp_rank < 0 || p->tp_rank >= p->tp) return ORC_ERR_SHAPE;
   if (p->shard_rows < 0 || p->hidden < 1 || p->num_tokens < 0) return ORC_ERR_SHAPE;
@@ -196,6 +229,9 @@ static int validate(const orc_problem* p, const void* partials, const void* resi
     if (p->out_dtype != ORC_F32 && p->out_dtype != ORC_BF16) return ORC_ERR_DTYPE;
   } else if (quant_mode == ORC_QUANT_STATIC_TENSOR || quant_mode == ORC_QUANT_DYNAMIC_TOKEN) {
     if (p->out_dtype != ORC_E4M3) return ORC_ERR_DTYPE;
+  } else if (quant_mode == ORC_QUANT_MX_BLOCK) {
+    if (p->out_dtype != ORC_E4M3 && p->out_dtype != ORC_E2M1) return ORC_ERR_DTYPE;
+    if (p->hidden % 32 != 0) return ORC_ERR_SHAPE;
   } else {
     return ORC_ERR_UNSUPPORTED;
   }
@@ -205,7 +241,8 @@ static int validate(const orc_problem* p, const void* partials, const void* resi
   if (rows == NULL && n_rows != S) return ORC_ERR_SHAPE;
   if (n_rows > 0) {
     if (!partials || !residual || !weight || !residual_out || !out) return ORC_ERR_NULL;
-    if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN && !out_scale) return ORC_ERR_NULL;
+    if ((quant_mode == ORC_QUANT_DYNAMIC_TOKEN || quant_mode == ORC_QUANT_MX_BLOCK) && !out_scale)
+      return ORC_ERR_NULL;
   }
   if (rows)
     for (int64_t i = 0; i < n_rows; ++i)
@@ -220,7 +257,7 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
                            const void* bias, float eps, int32_t quant_mode,
                            const void* deepstack, float static_scale,
                            int64_t n_rows, const int64_t* rows,
-                           void* residual_out, void* out, float* out_scale,
+                           void* residual_out, void* out, void* out_scale,
                            double* z_dbg, double* y_dbg) {
   int rc = validate(p, partials, residual, weight, quant_mode, deepstack, static_scale,
                     n_rows, rows, residual_out, out, out_scale);
@@ -241,8 +278,9 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
   const int64_t roff = (p->residual_rows == tp * S && tp > 1) ? r * S : 0;
   const int64_t doff = (deepstack && p->deepstack_rows == tp * S && tp > 1) ? r * S : 0;
 
-  const size_t oz = elt_size(p->out_dtype);
+  const size_t orow = row_bytes(p->out_dtype, H);
   const size_t az = elt_size(p->act_dtype);
+  const int64_t nblk = H / 32;
   double* z = (double*)malloc((size_t)H * sizeof(double));
   double* y = (double*)malloc((size_t)H * sizeof(double));
   if (!z || !y) {
@@ -256,8 +294,9 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
     if (s >= v) {
       /* padding row: every output is zero, no input is read */
       memset((char*)residual_out + (size_t)(i * H) * az, 0, (size_t)H * az);
-      memset((char*)out + (size_t)(i * H) * oz, 0, (size_t)H * oz);
-      if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN) out_scale[i] = 0.0f;
+      memset((char*)out + (size_t)i * orow, 0, orow);
+      if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN) ((float*)out_scale)[i] = 0.0f;
+      if (quant_mode == ORC_QUANT_MX_BLOCK) memset((uint8_t*)out_scale + i * nblk, 0, (size_t)nblk);
       if (z_dbg) memset(z_dbg + i * H, 0, (size_t)H * sizeof(double));
       if (y_dbg) memset(y_dbg + i * H, 0, (size_t)H * sizeof(double));
       continue;
@@ -290,12 +329,43 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
     } else if (quant_mode == ORC_QUANT_STATIC_TENSOR) {
       /* codes encode y / scale, scale a calibrated per-tensor constant */
       for (int64_t h = 0; h < H; ++h) store(out, ORC_E4M3, i * H + h, y[h] / (double)static_scale);
-    } else {
+    } else if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN) {
       /* per-token scale = max|y| / qmax, qmax = 448; codes encode y / scale */
       const float scale = (float)(amax / 448.0);
-      out_scale[i] = scale;
+      ((float*)out_scale)[i] = scale;
       for (int64_t h = 0; h < H; ++h)
         store(out, ORC_E4M3, i * H + h, scale > 0.0f ? y[h] / (double)scale : 0.0);
+    } else {
+      /* per-block scaling in the OCP microscaling form: for each block of 32
+       * consecutive elements, X = 2^e with e = floor(log2(max|y|)) - emax
+       * (emax = 8 for e4m3, 2 for e2m1; clamped to the E8M0 range [-127, 127];
+       * an all-zero block takes -127), elements encode y / X with saturation,
+       * the scale is stored as the E8M0 byte e + 127. */
+      const int emax = p->out_dtype == ORC_E4M3 ? 8 : 2;
+      for (int64_t b = 0; b < nblk; ++b) {
+        double bmax = 0.0;
+        for (int64_t h = 32 * b; h < 32 * b + 32; ++h)
+          if (fabs(y[h]) > bmax) bmax = fabs(y[h]);
+        int e = -127;
+        if (bmax > 0.0) {
+          int k;
+          (void)frexp(bmax, &k); /* bmax = m * 2^k, 0.5 <= m < 1: floor(log2 bmax) = k - 1 */
+          e = k - 1 - emax;
+        }
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+        ((uint8_t*)out_scale)[i * nblk + b] = (uint8_t)(e + 127);
+        for (int64_t h = 32 * b; h < 32 * b + 32; ++h) {
+          const double t = ldexp(y[h], -e);
+          if (p->out_dtype == ORC_E4M3) {
+            ((uint8_t*)out)[i * H + h] = orc_e4m3_from_double(t);
+          } else {
+            uint8_t* byte = (uint8_t*)out + (size_t)i * orow + (size_t)(h / 2);
+            const uint8_t c = orc_e2m1_from_double(t);
+            *byte = (h % 2 == 0) ? (uint8_t)((*byte & 0xF0) | c) : (uint8_t)((*byte & 0x0F) | (c << 4));
+          }
+        }
+      }
     }
 
     if (z_dbg) memcpy(z_dbg + i * H, z, (size_t)H * sizeof(double));
@@ -320,20 +390,27 @@ void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out) {
 
 /* AllGather followed by unpad ([SP/FC] §3.3: gather the shards along the
  * token dimension, then drop the padding rows): row t < T of the gathered
- * tensor is row t - q*S of shard q = t / S.  Bytes are copied unchanged. */
-int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t H, int64_t T, int32_t elt_bytes,
-                         const void* const* shards, const float* const* scales, void* out,
-                         float* out_scale) {
-  if (tp < 1 || S < 0 || H < 1 || T < 0 || T > (int64_t)tp * S) return ORC_ERR_SHAPE;
-  if (elt_bytes != 1 && elt_bytes != 2 && elt_bytes != 4) return ORC_ERR_DTYPE;
+ * tensor is row t - q*S of shard q = t / S, and the same for the rows of the
+ * scales.  Bytes are copied unchanged. */
+int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t row_bytes, int64_t T,
+                         const void* const* shards, int64_t scale_row_bytes,
+                         const void* const* scales, void* out, void* out_scale) {
+  if (tp < 1 || S < 0 || row_bytes < 1 || T < 0 || T > (int64_t)tp * S) return ORC_ERR_SHAPE;
+  if (scale_row_bytes < 0 || (scale_row_bytes > 0) != (scales != NULL)) return ORC_ERR_SHAPE;
   if (T > 0 && (!shards || !out)) return ORC_ERR_NULL;
   if (scales && !out_scale) return ORC_ERR_NULL;
-  const size_t row = (size_t)H * (size_t)elt_bytes;
   for (int64_t t = 0; t < T; ++t) {
     const int64_t q = t / S;
     const int64_t s = t - q * S;
-    memcpy((char*)out + (size_t)t * row, (const char*)shards[q] + (size_t)s * row, row);
-    if (scales) out_scale[t] = scales[q][s];
+    memcpy((char*)out + (size_t)(t * row_bytes), (const char*)shards[q] + (size_t)(s * row_bytes),
+           (size_t)row_bytes);
+    if (scales)
+      memcpy((char*)out_scale + (size_t)(t * scale_row_bytes),
+             (const char*)scales[q] + (size_t)(s * scale_row_bytes), (size_t)scale_row_bytes);
   }
   return ORC_OK;
+}
+
+void orc_e2m1_from_double_n(const double* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_from_double(x[i]);
 }

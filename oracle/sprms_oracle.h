@@ -26,13 +26,14 @@ extern "C" {
 #endif
 
 /* storage types understood by the oracle */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_E2M1 = 3 /* two per byte, even element low */ };
 
 /* output quantisation modes.  Dynamic per-tensor scaling is absent on
  * purpose: its scale needs the max over every rank's rows, so it cannot be
  * computed on one shard ([SPquant] §4, table of per-tensor quantisation
  * correctness). */
-enum { ORC_QUANT_NONE = 0, ORC_QUANT_STATIC_TENSOR = 1, ORC_QUANT_DYNAMIC_TOKEN = 2 };
+enum { ORC_QUANT_NONE = 0, ORC_QUANT_STATIC_TENSOR = 1, ORC_QUANT_DYNAMIC_TOKEN = 2,
+       ORC_QUANT_MX_BLOCK = 4 /* per 32-element block, power-of-two (E8M0) scales */ };
 
 enum {
   ORC_OK = 0,
@@ -50,7 +51,7 @@ typedef struct {
   int64_t num_tokens;     /* T: valid tokens over all ranks, 0 <= T <= tp*S */
   int32_t partial_dtype;  /* ORC_F32 | ORC_BF16 */
   int32_t act_dtype;      /* residual, deepstack, weight, bias, residual_out */
-  int32_t out_dtype;      /* ORC_F32 | ORC_BF16 (no quant), ORC_E4M3 (quant) */
+  int32_t out_dtype;      /* ORC_F32 | ORC_BF16 (no quant), ORC_E4M3 (quant), ORC_E2M1 (block) */
   int64_t residual_rows;  /* S (shard residual) or tp*S (replicated residual) */
   int64_t deepstack_rows; /* 0 (absent), S or tp*S */
 } orc_problem;
@@ -74,7 +75,8 @@ int orc_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp,
  * Outputs are compact, one row per requested row, in request order:
  *   residual_out [n_rows][H] act_dtype
  *   out          [n_rows][H] out_dtype
- *   out_scale    [n_rows] (dynamic mode; may be NULL otherwise)
+ *   out_scale    [n_rows] f32 (dynamic mode), [n_rows][H/32] E8M0 bytes (block
+ *                mode); may be NULL otherwise
  *   z_dbg, y_dbg [n_rows][H] doubles, optional: the pre-norm sum and the
  *                normalised value before output rounding (0 on pad rows).
  * Returns ORC_OK or a negative ORC_ERR_* code; on error nothing is written. */
@@ -83,14 +85,15 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
                            const void* bias, float eps, int32_t quant_mode,
                            const void* deepstack, float static_scale,
                            int64_t n_rows, const int64_t* rows,
-                           void* residual_out, void* out, float* out_scale,
+                           void* residual_out, void* out, void* out_scale,
                            double* z_dbg, double* y_dbg);
 
-/* AllGather + unpad of tp shard outputs [S][H] (elt_bytes each element) into
- * out [T][H]; scales [tp][S] -> out_scale [T] when scales != NULL. */
-int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t H, int64_t T, int32_t elt_bytes,
-                         const void* const* shards, const float* const* scales, void* out,
-                         float* out_scale);
+/* AllGather + unpad of tp shard outputs of S rows (row_bytes each) into out
+ * of T rows; shard scales of S rows (scale_row_bytes each) into out_scale of T
+ * rows when scales != NULL (scale_row_bytes 0 otherwise). */
+int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t row_bytes, int64_t T,
+                         const void* const* shards, int64_t scale_row_bytes,
+                         const void* const* scales, void* out, void* out_scale);
 
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
@@ -99,6 +102,9 @@ uint8_t orc_e4m3_from_double(double x);    /* clamp to +-448, nearest, ties to e
 double orc_e4m3_to_double(uint8_t code);   /* NaN for the two NaN codes */
 void orc_bf16_from_double_n(const double* x, int64_t n, uint16_t* out);
 void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out);
+uint8_t orc_e2m1_from_double(double x);    /* clamp to +-6, nearest, ties to even */
+double orc_e2m1_to_double(uint8_t code);
+void orc_e2m1_from_double_n(const double* x, int64_t n, uint8_t* out);
 
 #ifdef __cplusplus
 }

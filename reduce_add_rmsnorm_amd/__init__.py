@@ -22,9 +22,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsprms.so")
 
 # sp_dtype
-SP_F32, SP_BF16, SP_FP8_E4M3 = 0, 1, 2
-# sp_quant
-SP_QUANT_NONE, SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN = 0, 1, 2
+SP_F32, SP_BF16, SP_FP8_E4M3, SP_FP4_E2M1 = 0, 1, 2, 3
+# sp_quant (3 is reserved for dynamic per-tensor scaling and always rejected)
+SP_QUANT_NONE, SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN, SP_QUANT_MX_BLOCK = 0, 1, 2, 4
 # sp_status
 SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED, SP_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
@@ -65,6 +65,7 @@ class sp_gather_problem(C.Structure):
         ("shard_rows", C.c_int64),
         ("hidden", C.c_int64),
         ("num_tokens", C.c_int64),
+        ("scale_row_bytes", C.c_int64),
     ]
 
 
@@ -110,6 +111,8 @@ def _sp_dtype(dt: torch.dtype) -> int:
         return SP_BF16
     if dt in (torch.uint8, torch.float8_e4m3fn):
         return SP_FP8_E4M3
+    if dt == torch.float4_e2m1fn_x2:
+        return SP_FP4_E2M1
     raise TypeError(f"unsupported tensor dtype {dt}")
 
 
@@ -138,15 +141,19 @@ def _partials_stride(partials) -> int:
 
 
 def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deepstack=None,
-                 residual_out=None, valid_rows_only: bool = False) -> sp_problem:
+                 residual_out=None, valid_rows_only: bool = False,
+                 out_dtype: Optional[int] = None) -> sp_problem:
     """sp_problem from tensor shapes, strides and dtypes.  ``partials`` may be a
     [tp, S, H] view of a larger buffer (e.g. rows [r*S, (r+1)*S) of a
-    [tp, T_pad, H] tensor) as long as each partial's rows are packed."""
+    [tp, T_pad, H] tensor) as long as each partial's rows are packed.
+    ``out_dtype`` overrides the type inferred from ``out`` (e.g. SP_FP4_E2M1
+    for a uint8 [S, H/2] buffer of packed codes)."""
     tp, S, H = partials.shape
     stride = _partials_stride(partials)
     return sp_problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
                       partial_dtype=_sp_dtype(partials.dtype), act_dtype=_sp_dtype(residual.dtype),
-                      out_dtype=_sp_dtype(out.dtype), residual_rows=residual.shape[0],
+                      out_dtype=_sp_dtype(out.dtype) if out_dtype is None else out_dtype,
+                      residual_rows=residual.shape[0],
                       deepstack_rows=0 if deepstack is None else deepstack.shape[0],
                       residual_out=_addr(residual_out),
                       partial_stride=0 if stride == S * H else stride,
@@ -160,13 +167,16 @@ def _partials_addr(partials) -> int:
 
 def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack, out,
                           out_scale, *, tp_rank: int, num_tokens: int, residual_out=None,
-                          valid_rows_only: bool = False, stream=None) -> None:
+                          valid_rows_only: bool = False, out_dtype: Optional[int] = None,
+                          stream=None) -> None:
     """Enqueue the fused shard path (see include/sprms.h for the contract).
 
     partials [tp, S, H] f32/bf16; residual [S or tp*S, H]; weight, bias [H];
     deepstack None or [S or tp*S, H]; out [S, H] bf16/f32, or uint8 /
-    float8_e4m3fn for quant modes; out_scale None, [1] f32 (static) or [S]
-    f32 (dynamic); residual_out [S, H] or None (in place).  With
+    float8_e4m3fn for the e4m3 modes, or [S, H/2] uint8 / float4_e2m1fn_x2 for
+    block-scaled e2m1 (pass out_dtype=SP_FP4_E2M1 with uint8); out_scale None,
+    [1] f32 (static), [S] f32 (dynamic) or [S, H/32] uint8 E8M0 (block);
+    residual_out [S, H] or None (in place).  With
     ``valid_rows_only`` the padding rows of the outputs are left untouched
     (out may then be a row block of an unpadded gathered tensor).  Runs on
     ``stream`` (a torch stream or raw hipStream_t int; default: torch's
@@ -177,7 +187,7 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
         raise ValueError("partials must be a device tensor")
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out,
-                        valid_rows_only=valid_rows_only)
+                        valid_rows_only=valid_rows_only, out_dtype=out_dtype)
     with torch.cuda.device(partials.device):
         if stream is None:
             stream = torch.cuda.current_stream(partials.device)
@@ -188,7 +198,8 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
 
 
 def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, *,
-            tp_rank: int, num_tokens: int, residual_out=None, stream=None):
+            tp_rank: int, num_tokens: int, residual_out=None, out_dtype: Optional[int] = None,
+            stream=None):
     """Marshal the arguments of sp_reduce_add_rmsnorm once and return a
     no-argument callable that enqueues the call again (for timing loops).
     The tensors must stay alive and in place while the callable is used."""
@@ -196,7 +207,7 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
     if not partials.is_cuda:
         raise ValueError("partials must be a device tensor")
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
-                        deepstack=deepstack, residual_out=residual_out)
+                        deepstack=deepstack, residual_out=residual_out, out_dtype=out_dtype)
     if stream is None:
         stream = torch.cuda.current_stream(partials.device)
     handle = stream if isinstance(stream, int) else stream.cuda_stream
@@ -212,19 +223,24 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
 
 
 def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int,
-                        stream=None) -> None:
+                        dtype: Optional[int] = None, stream=None) -> None:
     """Gather tp shard outputs ([S, H] each, same dtype) into the unpadded
-    out [T, H] (and per-row scales [S] -> out_scale [T]); see include/sprms.h."""
+    out [T, H], and their scales ([S] f32 or [S, H/32] E8M0 bytes each) into
+    out_scale; see include/sprms.h.  Rows are copied as bytes: packed e2m1
+    shards may be given as uint8 [S, H/2] with dtype=SP_FP4_E2M1."""
     lib = load()
     tp = len(shards)
-    S, H = shards[0].shape
+    S, W = shards[0].shape
     for t in shards:
-        if t.shape != (S, H) or t.dtype != shards[0].dtype:
+        if t.shape != (S, W) or t.dtype != shards[0].dtype:
             raise ValueError("all shards must share shape and dtype")
     if not shards[0].is_cuda:
         raise ValueError("shards must be device tensors")
-    g = sp_gather_problem(tp=tp, dtype=_sp_dtype(shards[0].dtype), shard_rows=S, hidden=H,
-                          num_tokens=num_tokens)
+    dt = _sp_dtype(shards[0].dtype) if dtype is None else dtype
+    H = 2 * W if dt == SP_FP4_E2M1 else W
+    srow = 0 if shard_scales is None else shard_scales[0].nbytes // max(S, 1)
+    g = sp_gather_problem(tp=tp, dtype=dt, shard_rows=S, hidden=H, num_tokens=num_tokens,
+                          scale_row_bytes=srow)
     src = (C.c_void_p * tp)(*[_addr(t) for t in shards])
     ssrc = None
     if shard_scales is not None:

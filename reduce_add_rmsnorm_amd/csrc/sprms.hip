@@ -57,7 +57,8 @@ constexpr int max_threads() {
   return VPT == 1 ? kMaxThreads : kMaxThreadsMultiVec;
 }
 
-enum OutMode { OM_BF16 = 0, OM_F32 = 1, OM_FP8_STATIC = 2, OM_FP8_DYN = 3 };
+enum OutMode { OM_BF16 = 0, OM_F32 = 1, OM_FP8_STATIC = 2, OM_FP8_DYN = 3, OM_MX_FP8 = 4, OM_MX_FP4 = 5 };
+constexpr int kMxBlock = 32;  // elements per block scale (4 lanes x 8 elements)
 
 struct KArgs {
   const void* partials;   // [tp][S][H]
@@ -67,7 +68,7 @@ struct KArgs {
   const void* bias;       // [H] or nullptr
   const void* deepstack;  // this shard's deepstack rows or nullptr
   void* out;              // [S][H]
-  float* out_scale;       // static: [1] (read); dynamic: [S] (written)
+  void* out_scale;        // static: [1] f32 (read); dynamic: [S] f32, MX: [S][H/32] bytes (written)
   int64_t plane;          // elements between partial q's row and partial q+1's row
   int32_t H;
   int32_t nvec;           // H / 8
@@ -209,6 +210,24 @@ __device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStorePolicy);
 }
 
+// 8 fp32 -> 8 OCP e2m1 codes in one dword (element k in bits 4k..4k+3),
+// clamped to +-6 first; v_cvt_scalef32_pk_fp4_f32 with a unit scale.
+__device__ __forceinline__ uint32_t pack_e2m1(const float (&t)[kVec]) {
+  float c[kVec];
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) c[k] = fminf(fmaxf(t[k], -6.0f), 6.0f);
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c[0], c[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c[2], c[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c[4], c[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, c[6], c[7], 1.0f, 3);
+  return r;
+}
+
+__device__ __forceinline__ void store_e2m1(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStorePolicy);
+}
+
 // ------------------------------------------------------------- reductions
 
 // DPP move within a wavefront (row = 16 lanes); all controls used here read
@@ -236,6 +255,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
+// Max over the 4 lanes of a quad (lanes 4b..4b+3), in every lane of it.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  return fmaxf(v, dpp<kQuadSwap2>(v));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kQuadSwap1>(v));
   v = fmaxf(v, dpp<kQuadSwap2>(v));
@@ -251,7 +276,8 @@ template <int PT, int AT, int OM, int TP, int VPT>
 __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, float (&red)[3][kMaxWaves]) {
   using VP = Vec<PT>;
   using VA = Vec<AT>;
-  constexpr int kOutBytes = OM == OM_F32 ? 32 : OM == OM_BF16 ? 16 : 8;  // per 8 elements
+  constexpr int kOutBytes = OM == OM_F32 ? 32 : OM == OM_BF16 ? 16 : OM == OM_MX_FP4 ? 4 : 8;  // per 8 elements
+  constexpr bool kMx = OM == OM_MX_FP8 || OM == OM_MX_FP4;
 
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
@@ -283,10 +309,19 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
       VA::store_zero(r_res_out, vec[i] * VA::kBytes);
       if constexpr (OM == OM_BF16) Vec<SP_BF16>::store_zero(r_out, vec[i] * 16);
       if constexpr (OM == OM_F32) Vec<SP_F32>::store_zero(r_out, vec[i] * 32);
-      if constexpr (OM == OM_FP8_STATIC || OM == OM_FP8_DYN) store_e4m3(r_out, vec[i] * 8, u32x2{0, 0});
+      if constexpr (OM == OM_FP8_STATIC || OM == OM_FP8_DYN || OM == OM_MX_FP8)
+        store_e4m3(r_out, vec[i] * 8, u32x2{0, 0});
+      if constexpr (OM == OM_MX_FP4) store_e2m1(r_out, vec[i] * 4, 0u);
+      if constexpr (kMx) {
+        if ((tid & 3) == 0) {  // one scale byte per block of 32 = per quad of lanes
+          const rsrc_t r_sc = row_rsrc(static_cast<uint8_t*>(a.out_scale) + s * (a.H / kMxBlock),
+                                       static_cast<uint32_t>(a.H / kMxBlock));
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(0), r_sc, vec[i] / 4, 0, kStorePolicy);
+        }
+      }
     }
     if constexpr (OM == OM_FP8_DYN) {
-      if (tid == 0) a.out_scale[s] = 0.0f;
+      if (tid == 0) static_cast<float*>(a.out_scale)[s] = 0.0f;
     }
     return;
   }
@@ -317,7 +352,7 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
     for (int i = 0; i < VPT; ++i) rb[i] = VA::template load<kCachedPolicy>(r_b, vec[i] * VA::kBytes);
   }
   float static_scale = 1.0f;
-  if constexpr (OM == OM_FP8_STATIC) static_scale = a.out_scale[0];
+  if constexpr (OM == OM_FP8_STATIC) static_scale = static_cast<const float*>(a.out_scale)[0];
 
   if constexpr (TP > 0) {
     // ---- every load of the row in flight before the first add
@@ -432,6 +467,32 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
       if (live[i]) VO::store(r_out, vec[i] * VO::kBytes, z[i]);
+  } else if constexpr (kMx) {
+    // block of 32 = the 8-element vectors of one quad of lanes; rows hold
+    // whole blocks (H % 32 == 0), so a quad is entirely live or entirely not
+    constexpr int kEmax = OM == OM_MX_FP8 ? 8 : 2;
+    const rsrc_t r_sc = row_rsrc(static_cast<uint8_t*>(a.out_scale) + s * (a.H / kMxBlock),
+                                 static_cast<uint32_t>(a.H / kMxBlock));
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) m = fmaxf(m, fabsf(z[i][k]));
+      m = quad_max(m);
+      // floor(log2 m) = frexp exponent - 1 (exact, subnormals included)
+      int e = m > 0.0f ? __builtin_amdgcn_frexp_expf(m) - 1 - kEmax : -127;
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      float t[kVec];
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) t[k] = __builtin_ldexpf(z[i][k], -e);
+      if (live[i]) {
+        if constexpr (OM == OM_MX_FP8) store_e4m3(r_out, vec[i] * 8, pack_e4m3(t));
+        else store_e2m1(r_out, vec[i] * 4, pack_e2m1(t));
+        if ((tid & 3) == 0)
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(e + 127), r_sc, vec[i] / 4, 0,
+                                               kStorePolicy);
+      }
+    }
   } else {
     float inv;
     if constexpr (OM == OM_FP8_STATIC) {
@@ -457,7 +518,7 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
         for (int w = 0; w < nw; ++w) ymax = fmaxf(ymax, red[2][w]);
       }
       const float scale = ymax / 448.0f;
-      if (tid == 0) a.out_scale[s] = scale;
+      if (tid == 0) static_cast<float*>(a.out_scale)[s] = scale;
       inv = scale > 0.0f ? 1.0f / scale : 0.0f;
     }
 #pragma unroll
@@ -522,6 +583,8 @@ KFn pick_om(int om, int tp, int vpt) {
     case OM_F32: return pick_tp<PT, AT, OM_F32>(tp, vpt);
     case OM_FP8_STATIC: return pick_tp<PT, AT, OM_FP8_STATIC>(tp, vpt);
     case OM_FP8_DYN: return pick_tp<PT, AT, OM_FP8_DYN>(tp, vpt);
+    case OM_MX_FP8: return pick_tp<PT, AT, OM_MX_FP8>(tp, vpt);
+    case OM_MX_FP4: return pick_tp<PT, AT, OM_MX_FP4>(tp, vpt);
   }
   return nullptr;
 }
@@ -551,12 +614,12 @@ constexpr int kMaxTp = 64;
 
 struct GArgs {
   const char* src[kMaxTp];     // shard q's [S][H] output
-  const float* ssrc[kMaxTp];   // shard q's [S] scales (or all null)
+  const char* ssrc[kMaxTp];    // shard q's [S][scale_row_bytes] scales (or all null)
   char* out;                   // [T][H]
-  float* out_scale;            // [T] or null
+  char* out_scale;             // [T][scale_row_bytes] or null
   int64_t S;
-  uint32_t row_bytes;          // H * element size
-  int32_t has_scale;
+  uint32_t row_bytes;          // bytes of one output row
+  uint32_t scale_row_bytes;    // 0 when there are no scales
 };
 
 // One workgroup per gathered row t: shard q = t / S, row s = t - q*S, copied
@@ -578,7 +641,14 @@ __global__ void __launch_bounds__(kMaxThreads) gather_kernel(const GArgs a) {
       __builtin_amdgcn_raw_buffer_store_b64(v, dst, off, 0, kStorePolicy);
     }
   }
-  if (a.has_scale && threadIdx.x == 0) a.out_scale[t] = a.ssrc[q][s];
+  if (a.scale_row_bytes) {
+    const rsrc_t ssrc = row_rsrc(a.ssrc[q] + s * a.scale_row_bytes, a.scale_row_bytes);
+    const rsrc_t sdst = row_rsrc(a.out_scale + t * a.scale_row_bytes, a.scale_row_bytes);
+    for (uint32_t off = threadIdx.x; off < a.scale_row_bytes; off += blockDim.x) {
+      const uint8_t v = __builtin_amdgcn_raw_buffer_load_b8(ssrc, off, 0, kLoadPolicy);
+      __builtin_amdgcn_raw_buffer_store_b8(v, sdst, off, 0, kStorePolicy);
+    }
+  }
 }
 
 // ------------------------------------------------------------ host checks
@@ -594,6 +664,19 @@ int fail(int code, const char* fmt, ...) {
 }
 
 size_t elt_size(int dt) { return dt == SP_F32 ? 4 : dt == SP_BF16 ? 2 : dt == SP_FP8_E4M3 ? 1 : 0; }
+
+// bytes of one row of H elements (e2m1: two per byte); 0 for an unknown type
+size_t row_bytes_of(int dt, int64_t H) {
+  if (dt == SP_FP4_E2M1) return static_cast<size_t>(H) / 2;
+  return static_cast<size_t>(H) * elt_size(dt);
+}
+
+// bytes of out_scale per row, per quant mode (static: one f32 for the tensor)
+size_t scale_row_bytes_of(int quant_mode, int64_t H) {
+  if (quant_mode == SP_QUANT_DYNAMIC_TOKEN) return 4;
+  if (quant_mode == SP_QUANT_MX_BLOCK) return static_cast<size_t>(H) / kMxBlock;
+  return 0;
+}
 
 bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
 
@@ -611,7 +694,7 @@ struct Plan {
 
 int check(const sp_problem* p, const void* partials, const void* residual, const void* weight,
           const void* bias, float eps, int quant_mode, const void* deepstack, const void* out,
-          const float* out_scale, Plan* plan) {
+          const void* out_scale, Plan* plan) {
   if (!p) return fail(SP_ERR_NULL, "problem descriptor is NULL");
   if (p->tp < 1 || p->tp > 64) return fail(SP_ERR_SHAPE, "tp=%d outside [1, 64]", p->tp);
   if (p->tp_rank < 0 || p->tp_rank >= p->tp)
@@ -641,6 +724,13 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   } else if (quant_mode == SP_QUANT_STATIC_TENSOR || quant_mode == SP_QUANT_DYNAMIC_TOKEN) {
     if (p->out_dtype != SP_FP8_E4M3)
       return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_FP8_E4M3 with quant_mode=%d", p->out_dtype, quant_mode);
+  } else if (quant_mode == SP_QUANT_MX_BLOCK) {
+    if (p->out_dtype != SP_FP8_E4M3 && p->out_dtype != SP_FP4_E2M1)
+      return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_FP8_E4M3 or SP_FP4_E2M1 with block scaling",
+                  p->out_dtype);
+    if (H % kMxBlock != 0)
+      return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of %d with block scaling", (long long)H,
+                  kMxBlock);
   } else {
     return fail(SP_ERR_UNSUPPORTED,
                 "quant_mode=%d unsupported (dynamic per-tensor scaling is not shard-local)", quant_mode);
@@ -664,8 +754,8 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   if ((stride * static_cast<int64_t>(elt_size(p->partial_dtype))) % 16 != 0)
     return fail(SP_ERR_ALIGN, "partial_stride=%lld elements is not a multiple of 16 bytes",
                 (long long)stride);
-  if (out_scale && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
-    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", (const void*)out_scale);
+  if (out_scale && quant_mode != SP_QUANT_MX_BLOCK && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
+    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", out_scale);
 
   const int64_t r = p->tp_rank;
   int64_t v = p->num_tokens - r * S;
@@ -675,8 +765,7 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   plan->doff = (deepstack && p->deepstack_rows == tp * S) ? r * S : 0;
 
   // outputs must not overlap inputs (in-place residual excepted)
-  const size_t pe = elt_size(p->partial_dtype), ae = elt_size(p->act_dtype),
-               oe = elt_size(p->out_dtype);
+  const size_t pe = elt_size(p->partial_dtype), ae = elt_size(p->act_dtype);
   const size_t row_a = static_cast<size_t>(H) * ae;
   const char* res_used = static_cast<const char*>(residual) + plan->roff * row_a;
   struct Span {
@@ -691,7 +780,7 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
       {residual, static_cast<size_t>(p->residual_rows) * row_a},
   };
   const int64_t written_rows = (p->flags & SP_FLAG_VALID_ROWS_ONLY) ? plan->valid : S;
-  const size_t out_n = static_cast<size_t>(written_rows * H) * oe;
+  const size_t out_n = static_cast<size_t>(written_rows) * row_bytes_of(p->out_dtype, H);
   for (const Span& in : ins)
     if (overlap(out, out_n, in.p, in.n)) return fail(SP_ERR_SHAPE, "out overlaps an input");
   if (p->residual_out && p->residual_out != res_used) {
@@ -701,8 +790,8 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
         return fail(SP_ERR_SHAPE, "residual_out overlaps an input (pass NULL for in-place)");
     if (overlap(p->residual_out, ro_n, out, out_n)) return fail(SP_ERR_SHAPE, "residual_out overlaps out");
   }
-  if (quant_mode == SP_QUANT_DYNAMIC_TOKEN && out_scale) {
-    const size_t sn = static_cast<size_t>(written_rows) * 4;
+  if (scale_row_bytes_of(quant_mode, H) > 0 && out_scale) {
+    const size_t sn = static_cast<size_t>(written_rows) * scale_row_bytes_of(quant_mode, H);
     for (const Span& in : ins)
       if (overlap(out_scale, sn, in.p, in.n)) return fail(SP_ERR_SHAPE, "out_scale overlaps an input");
     if (overlap(out_scale, sn, out, out_n)) return fail(SP_ERR_SHAPE, "out_scale overlaps out");
@@ -718,14 +807,14 @@ extern "C" {
 
 int sp_validate(const sp_problem* p, const void* partials, const void* residual, const void* weight,
                 const void* bias, float eps, int quant_mode, const void* deepstack, const void* out,
-                const float* out_scale) {
+                const void* out_scale) {
   Plan plan;
   return check(p, partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, &plan);
 }
 
 int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
                           const void* weight, const void* bias, float eps, int quant_mode,
-                          const void* deepstack, void* out, float* out_scale, void* stream) {
+                          const void* deepstack, void* out, void* out_scale, void* stream) {
   Plan plan;
   int rc = check(p, partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, &plan);
   if (rc != SP_OK) return rc;
@@ -753,6 +842,7 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
 
   const int om = quant_mode == SP_QUANT_STATIC_TENSOR   ? OM_FP8_STATIC
                  : quant_mode == SP_QUANT_DYNAMIC_TOKEN ? OM_FP8_DYN
+                 : quant_mode == SP_QUANT_MX_BLOCK      ? (p->out_dtype == SP_FP4_E2M1 ? OM_MX_FP4 : OM_MX_FP8)
                  : p->out_dtype == SP_BF16              ? OM_BF16
                                                         : OM_F32;
   int vpt, nt;
@@ -770,7 +860,7 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
 }
 
 int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
-                        const float* const* shard_scales, void* out, float* out_scale,
+                        const void* const* shard_scales, void* out, void* out_scale,
                         void* stream) {
   if (!g) return fail(SP_ERR_NULL, "gather descriptor is NULL");
   if (g->tp < 1 || g->tp > kMaxTp) return fail(SP_ERR_SHAPE, "tp=%d outside [1, %d]", g->tp, kMaxTp);
@@ -780,21 +870,25 @@ int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
     return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, %d]", (long long)H, kMaxHidden);
   if (T < 0 || T > g->tp * S || T > INT32_MAX)
     return fail(SP_ERR_SHAPE, "num_tokens=%lld outside [0, tp*S=%lld]", (long long)T, (long long)(g->tp * S));
-  const size_t e = elt_size(g->dtype);
-  if (e == 0) return fail(SP_ERR_DTYPE, "dtype=%d unknown", g->dtype);
+  const size_t row_bytes = row_bytes_of(g->dtype, H);
+  if (row_bytes == 0) return fail(SP_ERR_DTYPE, "dtype=%d unknown", g->dtype);
+  if (g->dtype == SP_FP4_E2M1 && H % 16 != 0)
+    return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 16 for e2m1 rows", (long long)H);
+  const int64_t sb = g->scale_row_bytes;
+  if (sb < 0 || sb > 65536)
+    return fail(SP_ERR_SHAPE, "scale_row_bytes=%lld outside [0, 65536]", (long long)sb);
   if (T == 0) return SP_OK;
   if (!shards || !out) return fail(SP_ERR_NULL, "shards and out must be non-NULL");
-  if ((shard_scales == nullptr) != (out_scale == nullptr))
-    return fail(SP_ERR_NULL, "shard_scales and out_scale must both be given or both be NULL");
-  const size_t row_bytes = static_cast<size_t>(H) * e;
+  if ((shard_scales == nullptr) != (out_scale == nullptr) || (shard_scales == nullptr) != (sb == 0))
+    return fail(SP_ERR_NULL, "shard_scales, out_scale and scale_row_bytes must be all given or all none");
   // 16-byte accesses when rows are a multiple of 16 bytes, else 8-byte ones;
   // every row start must be aligned to the access width
   const int B = row_bytes % 16 == 0 ? 16 : 8;
   const uintptr_t amask = static_cast<uintptr_t>(B - 1);
   if (reinterpret_cast<uintptr_t>(out) & amask)
     return fail(SP_ERR_ALIGN, "out %p is not %d-byte aligned", out, B);
-  if (out_scale && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
-    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", (void*)out_scale);
+  if (out_scale && sb == 4 && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
+    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", out_scale);
   const size_t out_n = static_cast<size_t>(T) * row_bytes;
   GArgs ga;
   memset(&ga, 0, sizeof ga);
@@ -807,18 +901,18 @@ int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
     ga.src[q] = static_cast<const char*>(shards[q]);
     if (shard_scales) {
       if (!shard_scales[q]) return fail(SP_ERR_NULL, "shard_scales[%d] is NULL", q);
-      if (reinterpret_cast<uintptr_t>(shard_scales[q]) & 3u)
+      if (sb == 4 && (reinterpret_cast<uintptr_t>(shard_scales[q]) & 3u))
         return fail(SP_ERR_ALIGN, "shard_scales[%d] is not 4-byte aligned", q);
-      if (overlap(out_scale, static_cast<size_t>(T) * 4, shard_scales[q], static_cast<size_t>(S) * 4))
+      if (overlap(out_scale, static_cast<size_t>(T * sb), shard_scales[q], static_cast<size_t>(S * sb)))
         return fail(SP_ERR_SHAPE, "out_scale overlaps shard_scales[%d]", q);
-      ga.ssrc[q] = shard_scales[q];
+      ga.ssrc[q] = static_cast<const char*>(shard_scales[q]);
     }
   }
   ga.out = static_cast<char*>(out);
-  ga.out_scale = out_scale;
+  ga.out_scale = static_cast<char*>(out_scale);
   ga.S = S;
   ga.row_bytes = static_cast<uint32_t>(row_bytes);
-  ga.has_scale = shard_scales != nullptr;
+  ga.scale_row_bytes = static_cast<uint32_t>(sb);
   int nt = static_cast<int>((row_bytes / B + 63) / 64 * 64);
   nt = nt > kMaxThreads ? kMaxThreads : nt;
   void* args[] = {&ga};

@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN = 0, 1, 2
+QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK = 0, 1, 2, 4
 
 BASE_SEED = 20261202
 
@@ -55,6 +55,7 @@ class Workload:
     bias_sigma: float = 0.02
     eps: float = 1e-6
     seed_index: int = 0
+    fp4: bool = False          # block-scaled output with e2m1 elements (two per byte)
 
     @property
     def shard_rows(self) -> int:
@@ -72,11 +73,12 @@ class Workload:
         S, H, v = self.shard_rows, self.hidden, self.valid_rows(rank)
         pe = torch.tensor([], dtype=self.partial_dtype).element_size()
         ae = torch.tensor([], dtype=self.act_dtype).element_size()
-        oe = torch.tensor([], dtype=self.out_dtype).element_size()
+        out_row = H // 2 if self.fp4 else H * torch.tensor([], dtype=self.out_dtype).element_size()
         reads = v * H * (self.tp * pe + ae + (ae if self.deepstack else 0))
         reads += H * ae * (2 if self.bias else 1)
         reads += 4 if self.quant_mode == QUANT_STATIC_TENSOR else 0
-        writes = S * H * (ae + oe) + (4 * S if self.quant_mode == QUANT_DYNAMIC_TOKEN else 0)
+        scale_row = {QUANT_DYNAMIC_TOKEN: 4, QUANT_MX_BLOCK: H // 32}.get(self.quant_mode, 0)
+        writes = S * (H * ae + out_row + scale_row)
         return reads + writes
 
 

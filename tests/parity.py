@@ -21,6 +21,26 @@ from helpers import (bf16_bits_to_f64, bf16_round, e4m3_decode, e4m3_round, to_h
 from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR,
                                            Workload, make_inputs)
 
+QUANT_MX_BLOCK = sp.SP_QUANT_MX_BLOCK
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP e2m1 decode from the format definition (bias 1, subnormal m/2)."""
+    c = codes.astype(np.int64)
+    mag = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])[c & 7]
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_round(x: np.ndarray) -> np.ndarray:
+    return e2m1_decode(oracle.e2m1_from_double_array(x))
+
+
+def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
 CANARY = 0xA5
 
 
@@ -47,7 +67,7 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
              in_place: bool = False, out_dtype: Optional[torch.dtype] = None,
              static_scale: Optional[float] = None, shard_deepstack: bool = False,
              inputs: Optional[dict] = None, base_seed: Optional[int] = None,
-             require_exact_frac: float = 0.99) -> Result:
+             require_exact_frac: float = 0.99, fp4: bool = False) -> Result:
     S = w.shard_rows if S is None else S
     T = min(w.num_tokens, w.tp * S) if T is None else T
     kw = {} if base_seed is None else {"base_seed": base_seed}
@@ -64,7 +84,9 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     # host copies of every input before the call (the residual may be updated in place)
     h = {k: to_host(t) for k, t in x.items()}
 
-    out_buf, out = _canary_buffer(S, H, out_dtype, dev)
+    mx = quant == QUANT_MX_BLOCK
+    fp4 = fp4 and mx
+    out_buf, out = _canary_buffer(S, H // 2 if fp4 else H, out_dtype, dev)
     res_buf = res_out = None
     if not in_place:
         res_buf, res_out = _canary_buffer(S, H, w.act_dtype, dev)
@@ -75,10 +97,12 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     elif quant == QUANT_DYNAMIC_TOKEN:
         scale_buf = torch.full((S + 2,), float("nan"), dtype=torch.float32, device=dev)
         scale_t = scale_buf[1:S + 1]
+    elif mx:
+        scale_buf, scale_t = _canary_buffer(S, H // 32, torch.uint8, dev)
 
     sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], w.eps,
                              quant, x["deepstack"], out, scale_t, tp_rank=rank, num_tokens=T,
-                             residual_out=res_out)
+                             residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if fp4 else None)
     torch.cuda.synchronize()
 
     # ---- canaries and untouched memory (byte-exact)
@@ -102,6 +126,9 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     if quant == QUANT_DYNAMIC_TOKEN:
         sb = scale_buf.cpu().numpy()
         assert np.isnan(sb[0]) and np.isnan(sb[-1]), "out_scale canary"
+    if mx:
+        sb = scale_buf.cpu().numpy()
+        assert (sb[0] == CANARY).all() and (sb[-1] == CANARY).all(), "out_scale canary"
     for k in ("partials", "weight", "bias", "deepstack"):
         if x[k] is not None:
             np.testing.assert_array_equal(to_host(x[k]).view(np.uint8), h[k].view(np.uint8))
@@ -113,7 +140,8 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     ref = oracle.reduce_add_rmsnorm(
         h["partials"], h["residual"], h["weight"], h["bias"], w.eps, quant, h["deepstack"],
         tp_rank=rank, num_tokens=T,
-        out_dtype={torch.bfloat16: oracle.ORC_BF16, torch.float32: oracle.ORC_F32}.get(
+        out_dtype=oracle.ORC_E2M1 if fp4 else {torch.bfloat16: oracle.ORC_BF16,
+                                                torch.float32: oracle.ORC_F32}.get(
             out_dtype, oracle.ORC_E4M3),
         static_scale=static_scale if static_scale is not None else 1.0, rows=rows)
 
@@ -127,7 +155,7 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     if pad.any():
         assert not got_res[pad].view(np.uint8).any(), "residual_out not zero on padding rows"
         assert not got_out[pad].view(np.uint8).any(), "out not zero on padding rows"
-        if quant == QUANT_DYNAMIC_TOKEN:
+        if quant in (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK):
             assert not scale_t.cpu().numpy()[rows[pad]].any(), "out_scale not zero on padding rows"
     if not valid.any():
         return Result(rows, v, stats)
@@ -165,6 +193,9 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
         assert ok.all(), f"out outside bound at {np.argwhere(~ok)[:5].tolist()}"
         assert (np.abs(g - y) <= 1e-3 + 2.0 ** -7 * np.abs(y)).all(), "out outside 1e-3 + 2^-7|y|"
         stats["out_exact"] = float((go == ref["out"][valid]).mean())
+    elif mx:
+        _check_mx(stats, go, scale_t.cpu().numpy()[vr], ref["out"][valid], ref["out_scale"][valid],
+                  y, err_y, fp4)
     else:
         if quant == QUANT_STATIC_TENSOR:
             sc = np.full(len(vr), np.float64(np.float32(static_scale)))
@@ -212,3 +243,39 @@ def e4m3_step_of(v):
     a = np.minimum(np.abs(v), 448.0)
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
     return 2.0 ** (e - 3)
+
+
+def _check_mx(stats, got_codes, got_scale, ref_codes, ref_scale, y, err_y, fp4):
+    """Block-scaled outputs.  The block exponent is an integer decided by the
+    block max: accept the GPU's wherever the max lies within the y error bound
+    of a power of two; then every code must be a correct rounding of
+    y * 2^-e (the kernel's scaling by 2^-e is exact) within the bound."""
+    emax = 2 if fp4 else 8
+    n, H = y.shape
+    nb = H // 32
+    yb = np.abs(y).reshape(n, nb, 32)
+    eb = err_y.reshape(n, nb, 32)
+
+    def exp_of(m):
+        e = np.where(m > 0, np.floor(np.log2(np.where(m > 0, m, 1.0))) - emax, -127)
+        return np.clip(e, -127, 127)
+
+    e_lo = exp_of(np.maximum(yb - eb, 0).max(-1))
+    e_hi = exp_of((yb + eb).max(-1))
+    e_gpu = got_scale.astype(np.int64) - 127
+    ok = (e_gpu >= e_lo) & (e_gpu <= e_hi)
+    assert ok.all(), f"block exponents outside the bound at {np.argwhere(~ok)[:5].tolist()}"
+    stats["block_scale_exact"] = float((got_scale == ref_scale).mean())
+    codes = unpack_e2m1(got_codes) if fp4 else got_codes
+    own = unpack_e2m1(ref_codes) if fp4 else ref_codes
+    dec, rnd = (e2m1_decode, e2m1_round) if fp4 else (e4m3_decode, e4m3_round)
+    X = np.repeat(2.0 ** e_gpu, 32, axis=1)
+    t = y / X
+    err_t = err_y / X
+    g = dec(codes)
+    ok = within_rounding(g, t - err_t, t + err_t, rnd)
+    assert ok.all(), f"block codes outside bound at {np.argwhere(~ok)[:5].tolist()}"
+    same_e = np.repeat(got_scale == ref_scale, 32, axis=1)  # blocks on the oracle's exponent
+    diff = (codes != own) & ~((dec(own) == 0) & (g == 0)) & same_e
+    stats["codes_exact"] = 1.0 - float(diff.mean())
+    assert diff.mean() <= 1e-3, f"{diff.mean():.3%} of codes differ from the oracle's"

@@ -27,7 +27,8 @@ MUTATIONS = {
     "deepstack_chunk_off_by_one": ("p->deepstack_rows == tp * S && tp > 1) ? r * S : 0",
                                    "p->deepstack_rows == tp * S && tp > 1) ? r * S + 1 : 0"),
     "qmax_240": ("(float)(amax / 448.0)", "(float)(amax / 240.0)"),
-    "e4m3_no_tie_to_even": ("(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(0)"),
+    "e4m3_no_tie_to_even": ("for (int c = 0; c <= 0x7E; ++c) {\n    double err = fabs(orc_e4m3_to_double((uint8_t)c) - a);\n    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {",
+                            "for (int c = 0; c <= 0x7E; ++c) {\n    double err = fabs(orc_e4m3_to_double((uint8_t)c) - a);\n    if (err < best_err) {"),
     "bf16_ties_away": ("r = rint(a / spacing) * spacing;", "r = floor(a / spacing + 0.5) * spacing;"),
     "pad_rows_off_by_one": ("if (s >= v) {", "if (s > v) {"),
     "residual_not_added": ("z[h] = x + load(residual, p->act_dtype, (roff + s) * H + h);",
@@ -35,10 +36,16 @@ MUTATIONS = {
     "weight_ignored": ("y[h] = z[h] * rstd * load(weight, p->act_dtype, h);",
                        "y[h] = z[h] * rstd;"),
     "static_scale_multiplied": ("y[h] / (double)static_scale)", "y[h] * (double)static_scale)"),
-    "gather_rows_reversed": ("(const char*)shards[q] + (size_t)s * row, row);",
-                             "(const char*)shards[q] + (size_t)(S - 1 - s) * row, row);"),
-    "gather_scale_from_wrong_rank": ("if (scales) out_scale[t] = scales[q][s];",
-                                     "if (scales) out_scale[t] = scales[0][s];"),
+    "mx_emax_e2m1_off_by_one": ("const int emax = p->out_dtype == ORC_E4M3 ? 8 : 2;",
+                                "const int emax = p->out_dtype == ORC_E4M3 ? 8 : 3;"),
+    "mx_exponent_not_floor": ("e = k - 1 - emax;", "e = k - emax;"),
+    "mx_no_clamp_low": ("if (e < -127) e = -127;", "if (e < -150) e = -150;"),
+    "e2m1_no_tie_to_even": ("if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {\n      best = c;\n      best_err = err;\n    }\n  }\n  return (uint8_t)(best | (signbit(x) ? 0x8 : 0x0));",
+                            "if (err <= best_err) {\n      best = c;\n      best_err = err;\n    }\n  }\n  return (uint8_t)(best | (signbit(x) ? 0x8 : 0x0));"),
+    "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
+                             "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
+    "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",
+                                     "(const char*)scales[0] + (size_t)(s * scale_row_bytes)"),
 }
 
 

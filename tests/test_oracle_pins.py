@@ -21,6 +21,7 @@ from helpers import bf16_bits_to_f64, e4m3_decode, f32_to_bf16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 NONE, STATIC, DYNAMIC = oracle.QUANT_NONE, oracle.QUANT_STATIC_TENSOR, oracle.QUANT_DYNAMIC_TOKEN
+MX = oracle.QUANT_MX_BLOCK
 
 
 def f32(a):
@@ -220,22 +221,23 @@ def _all_ranks_setup(tp=4, T=10, T_pad=12, H=16, seed=5, deepstack=True):
     return full, R, D, w, b
 
 
-@pytest.mark.parametrize("quant", [NONE, STATIC, DYNAMIC])
-def test_reduce_scatter_plus_all_gather_equals_all_reduce(quant):
+@pytest.mark.parametrize("quant,od", [(NONE, oracle.ORC_BF16), (STATIC, oracle.ORC_E4M3),
+                                      (DYNAMIC, oracle.ORC_E4M3), (MX, oracle.ORC_E4M3),
+                                      (MX, oracle.ORC_E2M1)])
+def test_reduce_scatter_plus_all_gather_equals_all_reduce(quant, od):
     # [SP/FC] §2.2: RS followed by AG reproduces AR, and a per-token norm on
     # each shard equals the norm after gathering.  Path A: one shard holding
     # every row (the all-reduce path).  Path B: every rank on its own
     # contiguous slice (replicated residual and full deepstack chunked by
     # rank), concatenated in rank order and unpadded.
-    tp, T, T_pad, H = 4, 10, 12, 16
+    tp, T, T_pad, H = 4, 10, 12, 64
     full, R, D, w, b = _all_ranks_setup(tp, T, T_pad, H)
     S = T_pad // tp
-    kw = dict(quant=quant, static_scale=0.01, eps=1e-6,
-              out_dtype=oracle.ORC_BF16 if quant == NONE else oracle.ORC_E4M3)
+    kw = dict(quant=quant, static_scale=0.01, eps=1e-6, out_dtype=od)
     A = _run(full, R, w, b, deepstack=D, tp_rank=0, num_tokens=T, **kw)
     B = [_run(np.ascontiguousarray(full[:, r * S:(r + 1) * S]), R, w, b, deepstack=D, tp_rank=r,
               num_tokens=T, **kw) for r in range(tp)]
-    for key in ["residual_out", "out", "z", "y"] + (["out_scale"] if quant == DYNAMIC else []):
+    for key in ["residual_out", "out", "z", "y"] + (["out_scale"] if quant in (DYNAMIC, MX) else []):
         cat = np.concatenate([x[key] for x in B])
         np.testing.assert_array_equal(cat[:T], A[key][:T], err_msg=key)
         assert not np.any(cat[T:]), key  # padding rows of the last rank are zero
@@ -243,9 +245,10 @@ def test_reduce_scatter_plus_all_gather_equals_all_reduce(quant):
     for key in ("residual_out", "out"):
         g, _ = oracle.all_gather_unpad([x[key] for x in B], num_tokens=T)
         np.testing.assert_array_equal(g, A[key][:T], err_msg=key)
-    if quant == DYNAMIC:
+    if quant in (DYNAMIC, MX):
         g, gs = oracle.all_gather_unpad([x["out"] for x in B], [x["out_scale"] for x in B],
                                         num_tokens=T)
+        np.testing.assert_array_equal(g, A["out"][:T])
         np.testing.assert_array_equal(gs, A["out_scale"][:T])
 
 
@@ -459,3 +462,130 @@ def test_all_gather_unpad_worked_example():
     np.testing.assert_array_equal(out[:S, 1], np.arange(S))
     np.testing.assert_array_equal(out_scale[start:], scales[-1][:valid])
     assert T - start == valid and S - valid == g["pad_rows_total"]
+
+
+
+# ------------------------------------------------ block scaling (MX form)
+
+
+def test_e2m1_decode_matches_format_definition():
+    # OCP FP4 E2M1: bias 1, subnormal m/2, no NaN/inf: 0, .5, 1, 1.5, 2, 3, 4, 6
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert [oracle.e2m1_to_double(c) for c in range(8)] == mags
+    assert [oracle.e2m1_to_double(c | 8) for c in range(8)] == [-m for m in mags]
+
+
+@pytest.mark.parametrize("x,code", [
+    (0.0, 0), (-0.0, 8), (0.5, 1), (1.0, 2), (6.0, 7), (-6.0, 15), (100.0, 7), (-7.0, 15),
+    (0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),   # ties: even
+    (0.26, 1), (2.51, 5), (4.99, 6), (5.01, 7), (-1.3, 11),
+])
+def test_e2m1_encode_fixed_points(x, code):
+    assert oracle.e2m1_from_double(x) == code
+
+
+def test_e2m1_encode_brute_force_sweep():
+    grid = np.array([oracle.e2m1_to_double(c) for c in range(8)])
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.uniform(-7, 7, 5000), (grid[:-1] + grid[1:]) / 2])
+    codes = oracle.e2m1_from_double_array(x)
+    for xi, c in zip(x, codes):
+        a = min(abs(xi), 6.0)
+        d = np.abs(grid - a)
+        assert d[c & 7] == d.min()
+        assert (c >> 3) == (1 if np.signbit(xi) else 0)
+
+
+def _exact_rows(values):
+    """Partials/residual/gain such that y equals `values` exactly: z = +-1
+    everywhere (mean square 1, eps 0, rstd 1) and w = values * sign."""
+    values = np.asarray(values, np.float32)
+    n, H = values.shape
+    rng = np.random.default_rng(H)
+    sign = np.where(rng.random((n, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    # one shared gain: rows differ only through the sign pattern, so give
+    # every row its own call
+    return [(sign[i:i + 1][None], np.zeros((1, H), np.float32), values[i] * sign[i])
+            for i in range(n)]
+
+
+def _mx_row(values, od):
+    (P, R, w), = _exact_rows(np.asarray(values, np.float32)[None])
+    r = _run(P, R, w, quant=MX, eps=0.0, out_dtype=od)
+    return r
+
+
+def _e2m1_unpack(packed, H):
+    out = np.empty(H, np.uint8)
+    out[0::2] = packed & 0xF
+    out[1::2] = packed >> 4
+    return out
+
+
+def test_mx_fp4_closed_form_blocks():
+    blk = np.zeros(32, np.float32)
+    blk[:8] = [6.0, 3.0, -1.5, 0.5, 0.25, 0.75, -2.5, 5.0]
+    vals = np.concatenate([blk, blk * 2.0 ** 5, np.zeros(32, np.float32), blk * 2.0 ** -140])
+    r = _mx_row(vals, oracle.ORC_E2M1)
+    codes = _e2m1_unpack(r["out"][0], vals.size)
+    # block 0: max 6 -> floor(log2 6) - 2 = 0 -> X = 1 -> byte 127
+    # block 1: max 6*2^5 -> X = 2^5 -> byte 132, same codes
+    # block 2: all zero -> e = -127 -> byte 0, zero codes
+    # block 3: max 6*2^-140 -> e = -140 < -127 clamps -> byte 0; y*2^127 ~ 2^-13 -> 0
+    np.testing.assert_array_equal(r["out_scale"][0], [127, 132, 0, 0])
+    want = [7, 5, 11, 1, 0, 2, 12, 6] + [0] * 24
+    np.testing.assert_array_equal(codes[:32], want)
+    np.testing.assert_array_equal(codes[32:64], want)
+    assert not (codes[64:] & 7).any()
+
+
+def test_mx_fp8_closed_form_blocks():
+    blk = np.zeros(32, np.float32)
+    blk[:6] = [448.0, 300.0, -1.0, 0.5, 2.0 ** -9, 464.0 / 2]
+    sat = np.zeros(32, np.float32)
+    sat[:3] = [500.0, 260.0, -1.0]
+    vals = np.concatenate([blk, blk / 256, sat])
+    r = _mx_row(vals, oracle.ORC_E4M3)
+    # block 0: max 448 -> floor(log2 448) - 8 = 0 -> byte 127, codes of the values
+    # block 1: the same / 256 -> e = -8 -> byte 119, same codes
+    # block 2: max 500 -> e = 0, 500 saturates to 448
+    np.testing.assert_array_equal(r["out_scale"][0], [127, 119, 127])
+    c = r["out"][0]
+    np.testing.assert_array_equal(c[:6], [0x7E, 0x79, 0xB8, 0x30, 0x01, 0x76])  # 300 -> 288
+    np.testing.assert_array_equal(c[32:38], c[:6])
+    np.testing.assert_array_equal(c[64:67], [0x7E, 0x78, 0xB8])
+
+
+def test_mx_block_scale_invariance():
+    # scaling a whole row by 2^k moves every E8M0 byte by k and keeps the codes
+    rng = np.random.default_rng(10)
+    vals = (rng.normal(0, 1, 128) * np.repeat([1.0, 2.0 ** -3, 7.0, 1e-3], 32)).astype(np.float32)
+    for od in (oracle.ORC_E4M3, oracle.ORC_E2M1):
+        a = _mx_row(vals, od)
+        c = _mx_row(vals * 2.0 ** 6, od)
+        np.testing.assert_array_equal(c["out"], a["out"])
+        np.testing.assert_array_equal(c["out_scale"].astype(int), a["out_scale"].astype(int) + 6)
+
+
+def test_mx_codes_decode_within_half_a_step():
+    # every block: codes decode, times 2^e, to within half an element step of y
+    rng = np.random.default_rng(11)
+    vals = rng.normal(0, 1, 256).astype(np.float32)
+    for od, emax in ((oracle.ORC_E4M3, 8), (oracle.ORC_E2M1, 2)):
+        r = _mx_row(vals, od)
+        e = r["out_scale"][0].astype(int) - 127
+        codes = r["out"][0] if od == oracle.ORC_E4M3 else _e2m1_unpack(r["out"][0], 256)
+        dec = e4m3_decode(codes) if od == oracle.ORC_E4M3 else np.array(
+            [oracle.e2m1_to_double(c) for c in codes])
+        for b in range(8):
+            blk = vals[32 * b:32 * b + 32].astype(np.float64)
+            assert e[b] == int(np.floor(np.log2(np.abs(blk).max()))) - emax
+            t = blk / 2.0 ** e[b]
+            if od == oracle.ORC_E4M3:
+                step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -6))) - 3)
+                tmax = 448.0
+            else:
+                step = np.where(np.abs(t) < 2, 0.5, np.where(np.abs(t) < 4, 1.0, 2.0))
+                tmax = 6.0
+            d = dec[32 * b:32 * b + 32]
+            assert (np.abs(d - np.clip(t, -tmax, tmax)) <= step / 2 + 1e-12).all()
