@@ -10,7 +10,8 @@
  * §2.1-§2.3; vLLM SP / AsyncTP / quantisation notes, beaiera.top, §1-§4).
  * For one rank's shard this library computes, in one kernel launch:
  *
- *   z[s][h]  = ((sum over q=0..tp-1 of P[q][s][h]) + D[s][h]) + R[s][h]   (fp32, rank order)
+ *   z[s][h]  = ((sum over q=0..tp-1 of c*P[q][s][h]) + D[s][h]) + R[s][h]  (fp32, rank order,
+ *              c = partial_scale, 1 unless set)
  *   residual_out[s][h] = z[s][h]                                         (rounded to act dtype)
  *   y[s][h]  = z[s][h] * rsqrt(mean_h z[s][h]^2 + eps) * w[h] (+ b[h])
  *   out      = y (bf16 / f32), or FP8 e4m3 codes of y / scale with
@@ -88,6 +89,10 @@ typedef struct {
                              (a packed [tp][S][H] block).  T_pad*H lets partials be the rank's
                              row block of tp full [T_pad][H] partial tensors held in one buffer. */
   int32_t flags;          /* 0 or SP_FLAG_VALID_ROWS_ONLY */
+  float partial_scale;    /* every partial is multiplied by this factor before it joins the
+                             sum (the DSA-CP o_proj finalize scales its output before the
+                             reduction: vllm-ascend PR #18671 walkthrough, §5.3); 0 is read as
+                             1; must be finite */
 } sp_problem;
 
 /* Flag: write out, out_scale and residual_out for the shard's valid rows
@@ -179,6 +184,41 @@ typedef struct {
 int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
                         const void* const* shard_scales, void* out, void* out_scale,
                         void* stream);
+
+/* Problem descriptor of sp_fc2_regroup (host memory, read during the call only). */
+typedef struct {
+  int32_t global_tp;  /* G, ranks of the tensor-parallel group, 2 <= G <= 64 */
+  int32_t otp;        /* ranks that compute o_proj together, 1 <= otp < G, G % otp == 0 */
+  int32_t dtype;      /* element type: SP_F32 | SP_BF16 | SP_FP8_E4M3 */
+  int32_t reserved;   /* 0 */
+  int64_t tokens;     /* N, N % G == 0, 0 <= N < 2^31 */
+  int64_t cols;       /* C = H / G, feature columns held by each rank, C * elt % 4 == 0 */
+} sp_fc2_problem;
+
+/*
+ * sp_fc2_regroup -- the FlashComm2 input regrouping of o_proj (vllm-ascend SP
+ * / FlashComm guide, §4.3-4.4): with odp = G / otp, the G ranks form ODP
+ * groups of odp consecutive ranks; the N tokens form G equal segments; rank
+ * r = g*odp + j ends up holding token segments j + k*odp (k = 0..otp-1, in
+ * that order, the "reorganised batch ids") with the feature columns of the
+ * odp ranks of its ODP group side by side, i.e. [N/odp][odp*C].  Ranks with
+ * the same j form an OTP group: they hold the same tokens, different feature
+ * columns, and their o_proj partials reduce-scatter so that rank r keeps
+ * segment r, the sequence-parallel layout.
+ *
+ *   f    problem descriptor (host)
+ *   src  host array of G device pointers, rank q's [N][C] input (its feature
+ *        columns of every token); on a node, peer-mapped buffers
+ *   dst  host array of G device pointers, rank r's [N/odp][odp*C] output
+ *
+ * Pointers 16-byte aligned (4-byte when C * elt % 16 != 0); a dst must not
+ * overlap any src or another dst.  Bytes are copied unchanged, one workgroup
+ * per destination row, so otp * N times the workgroup size (up to 1024) must
+ * stay below 2^32.  N == 0 enqueues nothing.  Same error convention as
+ * sp_reduce_add_rmsnorm.
+ */
+int sp_fc2_regroup(const sp_fc2_problem* f, const void* const* src, void* const* dst,
+                   void* stream);
 
 /*
  * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.

@@ -26,6 +26,8 @@ from .oracle import (  # noqa: F401
     e4m3_from_double,
     e4m3_from_double_array,
     e4m3_to_double,
+    fc2_batch_ids,
+    fc2_regroup,
     reduce_add_rmsnorm,
     shard_geometry,
 )

@@ -44,6 +44,7 @@ class _Problem(C.Structure):
         ("out_dtype", C.c_int32),
         ("residual_rows", C.c_int64),
         ("deepstack_rows", C.c_int64),
+        ("partial_scale", C.c_double),
     ]
 
 
@@ -82,6 +83,10 @@ def _load():
     lib.orc_all_gather_unpad.argtypes = [i32, i64, i64, i64, C.POINTER(vp), i64, C.POINTER(vp),
                                          vp, vp]
     lib.orc_all_gather_unpad.restype = C.c_int
+    lib.orc_fc2_batch_ids.argtypes = [i32, i32, vp]
+    lib.orc_fc2_batch_ids.restype = C.c_int
+    lib.orc_fc2_regroup.argtypes = [i32, i32, i64, i64, i32, C.POINTER(vp), C.POINTER(vp)]
+    lib.orc_fc2_regroup.restype = C.c_int
     lib.orc_e2m1_from_double.argtypes = [C.c_double]
     lib.orc_e2m1_from_double.restype = C.c_uint8
     lib.orc_e2m1_to_double.argtypes = [C.c_uint8]
@@ -121,7 +126,7 @@ def shard_geometry(num_tokens: int, num_tokens_pad: int, tp: int, rank: int):
 
 def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack=None, *,
                        tp_rank, num_tokens, out_dtype=ORC_BF16, static_scale=1.0, rows=None,
-                       want_debug=True):
+                       want_debug=True, partial_scale=1.0):
     """Run the oracle on host arrays.
 
     partials [tp, S, H]; residual [S or tp*S, H]; weight/bias [H];
@@ -146,7 +151,8 @@ def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepst
     prob = _Problem(tp=tp, tp_rank=tp_rank, shard_rows=S, hidden=H, num_tokens=num_tokens,
                     partial_dtype=_dtype_code(partials), act_dtype=act, out_dtype=out_dtype,
                     residual_rows=residual.shape[0],
-                    deepstack_rows=0 if deepstack is None else deepstack.shape[0])
+                    deepstack_rows=0 if deepstack is None else deepstack.shape[0],
+                    partial_scale=float(partial_scale))
     if rows is None:
         n = S
         rows_arr = None
@@ -243,3 +249,31 @@ def e2m1_from_double_array(x) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint8)
     _load().orc_e2m1_from_double_n(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def fc2_batch_ids(G: int, otp: int):
+    """Reorganised batch ids: for each destination position j of an ODP group,
+    the token segments it receives."""
+    odp = G // otp
+    ids = np.zeros((odp, otp), dtype=np.int32)
+    rc = _load().orc_fc2_batch_ids(G, otp, _ptr(ids))
+    if rc != 0:
+        raise OracleError(f"orc_fc2_batch_ids failed: {rc}")
+    return ids.tolist()
+
+
+def fc2_regroup(srcs, otp: int):
+    """Regroup G host arrays [N, C] (rank q's features of all tokens) into G
+    arrays [N/odp, odp*C]."""
+    lib = _load()
+    srcs = [np.ascontiguousarray(a) for a in srcs]
+    G = len(srcs)
+    N, Cc = srcs[0].shape
+    odp = G // otp
+    dsts = [np.zeros((N // odp, odp * Cc), dtype=srcs[0].dtype) for _ in range(G)]
+    sp_ = (C.c_void_p * G)(*[a.ctypes.data for a in srcs])
+    dp_ = (C.c_void_p * G)(*[a.ctypes.data for a in dsts])
+    rc = lib.orc_fc2_regroup(G, otp, N, Cc, srcs[0].dtype.itemsize, sp_, dp_)
+    if rc != 0:
+        raise OracleError(f"orc_fc2_regroup failed: {rc}")
+    return dsts

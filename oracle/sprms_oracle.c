@@ -215,6 +215,7 @@ static int validate(const orc_problem* p, const void* partials, const void* resi
   if (!p) return ORC_ERR_NULL;
   if (p->tp < 1 || p->tp_rank < 0 || p->tp_rank >= p->tp) return ORC_ERR_SHAPE;
   if (p->shard_rows < 0 || p->hidden < 1 || p->num_tokens < 0) return ORC_ERR_SHAPE;
+  if (!isfinite(p->partial_scale)) return ORC_ERR_SHAPE;
   if (p->num_tokens > (int64_t)p->tp * p->shard_rows) return ORC_ERR_SHAPE;
   int64_t S = p->shard_rows;
   if (p->residual_rows != S && p->residual_rows != (int64_t)p->tp * S) return ORC_ERR_SHAPE;
@@ -302,10 +303,13 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
       continue;
     }
 
-    /* z = ((sum over ranks of the partials) + deepstack) + residual */
+    /* z = ((sum over ranks of the scaled partials) + deepstack) + residual; the
+     * DSA-CP o_proj finalize multiplies each rank's output by a factor before
+     * the reduction ([PR18671] §5.3) */
     for (int64_t h = 0; h < H; ++h) {
       double x = 0.0;
-      for (int64_t q = 0; q < tp; ++q) x += load(partials, p->partial_dtype, (q * S + s) * H + h);
+      for (int64_t q = 0; q < tp; ++q)
+        x += p->partial_scale * load(partials, p->partial_dtype, (q * S + s) * H + h);
       if (deepstack) x += load(deepstack, p->act_dtype, (doff + s) * H + h);
       z[h] = x + load(residual, p->act_dtype, (roff + s) * H + h);
       store(residual_out, p->act_dtype, i * H + h, z[h]);
@@ -413,4 +417,53 @@ int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t row_bytes, int64_t T,
 
 void orc_e2m1_from_double_n(const double* x, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_from_double(x[i]);
+}
+
+/* -------------------------------------------------- FlashComm2 regrouping */
+
+/* [SP/FC] §4.4: with odp = G / otp, destination position j of an ODP group
+ * receives the token segments j, j + odp, j + 2*odp, ... (otp of them): for
+ * G = 4, otp = 2 this is [[0, 2], [1, 3]].  ids is [odp][otp]. */
+int orc_fc2_batch_ids(int32_t G, int32_t otp, int32_t* ids) {
+  if (G < 2 || otp < 1 || otp >= G || G % otp != 0 || !ids) return ORC_ERR_SHAPE;
+  const int odp = G / otp;
+  for (int j = 0; j < odp; ++j)
+    for (int k = 0; k < otp; ++k) ids[j * otp + k] = j + k * odp;
+  return ORC_OK;
+}
+
+/* [SP/FC] §4.4, steps 1-3 written out: rank q holds features q of all N
+ * tokens ([N][C], elt bytes each).  Each rank splits its tokens into G
+ * segments and sends destination j of its ODP group (the odp consecutive
+ * ranks g*odp .. g*odp+odp-1) the segments of batch ids row j; destination
+ * r = g*odp + j concatenates what it receives along the features, in the
+ * order of the senders: out[r] is [N/odp][odp*C]. */
+int orc_fc2_regroup(int32_t G, int32_t otp, int64_t N, int64_t C, int32_t elt,
+                    const void* const* src, void* const* dst) {
+  if (G < 2 || otp < 1 || otp >= G || G % otp != 0 || N < 0 || N % G != 0 || C < 1)
+    return ORC_ERR_SHAPE;
+  if (N > 0 && (!src || !dst)) return ORC_ERR_NULL;
+  const int odp = G / otp;
+  const int64_t seg = N / G;
+  int32_t ids[64 * 64];
+  if (G > 64) return ORC_ERR_SHAPE;
+  orc_fc2_batch_ids(G, otp, ids);
+  const size_t piece = (size_t)C * (size_t)elt;
+  for (int g = 0; g < G / odp; ++g)
+    for (int j = 0; j < odp; ++j) {
+      const int r = g * odp + j;
+      int64_t t = 0; /* destination row */
+      for (int k = 0; k < otp; ++k) {
+        const int segment = ids[j * otp + k];
+        for (int64_t u = 0; u < seg; ++u, ++t) {
+          const int64_t n = segment * seg + u; /* source token */
+          for (int i = 0; i < odp; ++i) {     /* sender i of the ODP group */
+            const char* from = (const char*)src[g * odp + i] + (size_t)n * piece;
+            char* to = (char*)dst[r] + (size_t)t * piece * odp + (size_t)i * piece;
+            memcpy(to, from, piece);
+          }
+        }
+      }
+    }
+  return ORC_OK;
 }

@@ -54,6 +54,7 @@ typedef struct {
   int32_t out_dtype;      /* ORC_F32 | ORC_BF16 (no quant), ORC_E4M3 (quant), ORC_E2M1 (block) */
   int64_t residual_rows;  /* S (shard residual) or tp*S (replicated residual) */
   int64_t deepstack_rows; /* 0 (absent), S or tp*S */
+  double partial_scale;   /* factor applied to every partial before the sum (1 = none) */
 } orc_problem;
 
 /* Shard layout of [PR18671] §2 and §5.2: contiguous rank shards of
@@ -94,6 +95,12 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
 int orc_all_gather_unpad(int32_t tp, int64_t S, int64_t row_bytes, int64_t T,
                          const void* const* shards, int64_t scale_row_bytes,
                          const void* const* scales, void* out, void* out_scale);
+
+/* FlashComm2 reorganised batch ids ([odp][otp]) and input regrouping of G
+ * ranks' [N][C] inputs into [N/odp][odp*C] per rank. */
+int orc_fc2_batch_ids(int32_t G, int32_t otp, int32_t* ids);
+int orc_fc2_regroup(int32_t G, int32_t otp, int64_t N, int64_t C, int32_t elt,
+                    const void* const* src, void* const* dst);
 
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */

@@ -29,8 +29,8 @@ SP_QUANT_NONE, SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN, SP_QUANT_MX_BLOCK
 SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED, SP_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 
-EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_shard_geometry",
-            "sp_error_string", "sp_last_error")
+EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_fc2_regroup",
+            "sp_shard_geometry", "sp_error_string", "sp_last_error")
 SP_FLAG_VALID_ROWS_ONLY = 1
 
 
@@ -55,6 +55,7 @@ class sp_problem(C.Structure):
         ("residual_out", C.c_void_p),
         ("partial_stride", C.c_int64),
         ("flags", C.c_int32),
+        ("partial_scale", C.c_float),
     ]
 
 
@@ -66,6 +67,17 @@ class sp_gather_problem(C.Structure):
         ("hidden", C.c_int64),
         ("num_tokens", C.c_int64),
         ("scale_row_bytes", C.c_int64),
+    ]
+
+
+class sp_fc2_problem(C.Structure):
+    _fields_ = [
+        ("global_tp", C.c_int32),
+        ("otp", C.c_int32),
+        ("dtype", C.c_int32),
+        ("reserved", C.c_int32),
+        ("tokens", C.c_int64),
+        ("cols", C.c_int64),
     ]
 
 
@@ -93,6 +105,8 @@ def load(build_if_missing: bool = False):
     lib.sp_all_gather_unpad.argtypes = [C.POINTER(sp_gather_problem), C.POINTER(vp),
                                         C.POINTER(vp), vp, vp, vp]
     lib.sp_all_gather_unpad.restype = C.c_int
+    lib.sp_fc2_regroup.argtypes = [C.POINTER(sp_fc2_problem), C.POINTER(vp), C.POINTER(vp), vp]
+    lib.sp_fc2_regroup.restype = C.c_int
     lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
                                       C.POINTER(i64)]
     lib.sp_shard_geometry.restype = C.c_int
@@ -142,7 +156,7 @@ def _partials_stride(partials) -> int:
 
 def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deepstack=None,
                  residual_out=None, valid_rows_only: bool = False,
-                 out_dtype: Optional[int] = None) -> sp_problem:
+                 out_dtype: Optional[int] = None, partial_scale: float = 1.0) -> sp_problem:
     """sp_problem from tensor shapes, strides and dtypes.  ``partials`` may be a
     [tp, S, H] view of a larger buffer (e.g. rows [r*S, (r+1)*S) of a
     [tp, T_pad, H] tensor) as long as each partial's rows are packed.
@@ -157,7 +171,8 @@ def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deep
                       deepstack_rows=0 if deepstack is None else deepstack.shape[0],
                       residual_out=_addr(residual_out),
                       partial_stride=0 if stride == S * H else stride,
-                      flags=SP_FLAG_VALID_ROWS_ONLY if valid_rows_only else 0)
+                      flags=SP_FLAG_VALID_ROWS_ONLY if valid_rows_only else 0,
+                      partial_scale=partial_scale)
 
 
 def _partials_addr(partials) -> int:
@@ -168,7 +183,7 @@ def _partials_addr(partials) -> int:
 def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepstack, out,
                           out_scale, *, tp_rank: int, num_tokens: int, residual_out=None,
                           valid_rows_only: bool = False, out_dtype: Optional[int] = None,
-                          stream=None) -> None:
+                          partial_scale: float = 1.0, stream=None) -> None:
     """Enqueue the fused shard path (see include/sprms.h for the contract).
 
     partials [tp, S, H] f32/bf16; residual [S or tp*S, H]; weight, bias [H];
@@ -178,7 +193,8 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
     [1] f32 (static), [S] f32 (dynamic) or [S, H/32] uint8 E8M0 (block);
     residual_out [S, H] or None (in place).  With
     ``valid_rows_only`` the padding rows of the outputs are left untouched
-    (out may then be a row block of an unpadded gathered tensor).  Runs on
+    (out may then be a row block of an unpadded gathered tensor).
+    ``partial_scale`` multiplies every partial before the sum.  Runs on
     ``stream`` (a torch stream or raw hipStream_t int; default: torch's
     current stream on partials' device).
     """
@@ -187,7 +203,8 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
         raise ValueError("partials must be a device tensor")
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out,
-                        valid_rows_only=valid_rows_only, out_dtype=out_dtype)
+                        valid_rows_only=valid_rows_only, out_dtype=out_dtype,
+                        partial_scale=partial_scale)
     with torch.cuda.device(partials.device):
         if stream is None:
             stream = torch.cuda.current_stream(partials.device)
@@ -250,6 +267,28 @@ def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int
             stream = torch.cuda.current_stream(shards[0].device)
         handle = stream if isinstance(stream, int) else stream.cuda_stream
         _check(lib.sp_all_gather_unpad(C.byref(g), src, ssrc, _addr(out), _addr(out_scale), handle))
+
+
+def sp_fc2_regroup(srcs, dsts, *, otp: int, stream=None) -> None:
+    """FlashComm2 o_proj input regrouping of G ranks: srcs[q] [N, C] ->
+    dsts[r] [N/odp, odp*C], odp = G/otp; see include/sprms.h."""
+    lib = load()
+    G = len(srcs)
+    N, Cc = srcs[0].shape
+    for t in srcs:
+        if t.shape != (N, Cc) or t.dtype != srcs[0].dtype:
+            raise ValueError("all sources must share shape and dtype")
+    if len(dsts) != G:
+        raise ValueError("one destination per rank")
+    f = sp_fc2_problem(global_tp=G, otp=otp, dtype=_sp_dtype(srcs[0].dtype), reserved=0,
+                       tokens=N, cols=Cc)
+    src = (C.c_void_p * G)(*[_addr(t) for t in srcs])
+    dst = (C.c_void_p * G)(*[_addr(t) for t in dsts])
+    with torch.cuda.device(srcs[0].device):
+        if stream is None:
+            stream = torch.cuda.current_stream(srcs[0].device)
+        handle = stream if isinstance(stream, int) else stream.cuda_stream
+        _check(lib.sp_fc2_regroup(C.byref(f), src, dst, handle))
 
 
 def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,

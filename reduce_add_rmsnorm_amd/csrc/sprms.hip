@@ -75,6 +75,7 @@ struct KArgs {
   int32_t valid;          // rows [0, valid) are real tokens
   int32_t tp;
   float eps;
+  float pscale;           // factor applied to every partial before the sum
 };
 
 // ------------------------------------------------------------ element I/O
@@ -139,6 +140,13 @@ struct Vec<SP_BF16> {
     f[4] += bf16_lo(v.z); f[5] += bf16_hi(v.z);
     f[6] += bf16_lo(v.w); f[7] += bf16_hi(v.w);
   }
+  // f += c * v with one rounding (c = 1 gives exactly f + v)
+  static __device__ __forceinline__ void add_scaled(const raw& v, float c, float (&f)[kVec]) {
+    f[0] = fmaf(c, bf16_lo(v.x), f[0]); f[1] = fmaf(c, bf16_hi(v.x), f[1]);
+    f[2] = fmaf(c, bf16_lo(v.y), f[2]); f[3] = fmaf(c, bf16_hi(v.y), f[3]);
+    f[4] = fmaf(c, bf16_lo(v.z), f[4]); f[5] = fmaf(c, bf16_hi(v.z), f[5]);
+    f[6] = fmaf(c, bf16_lo(v.w), f[6]); f[7] = fmaf(c, bf16_hi(v.w), f[7]);
+  }
   static __device__ __forceinline__ void unpack(const raw& v, float (&f)[kVec]) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
     f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
@@ -172,6 +180,13 @@ struct Vec<SP_F32> {
     f[2] += __uint_as_float(v.a.z); f[3] += __uint_as_float(v.a.w);
     f[4] += __uint_as_float(v.b.x); f[5] += __uint_as_float(v.b.y);
     f[6] += __uint_as_float(v.b.z); f[7] += __uint_as_float(v.b.w);
+  }
+  // f += c * v with one rounding (c = 1 gives exactly f + v)
+  static __device__ __forceinline__ void add_scaled(const raw& v, float c, float (&f)[kVec]) {
+    f[0] = fmaf(c, __uint_as_float(v.a.x), f[0]); f[1] = fmaf(c, __uint_as_float(v.a.y), f[1]);
+    f[2] = fmaf(c, __uint_as_float(v.a.z), f[2]); f[3] = fmaf(c, __uint_as_float(v.a.w), f[3]);
+    f[4] = fmaf(c, __uint_as_float(v.b.x), f[4]); f[5] = fmaf(c, __uint_as_float(v.b.y), f[5]);
+    f[6] = fmaf(c, __uint_as_float(v.b.z), f[6]); f[7] = fmaf(c, __uint_as_float(v.b.w), f[7]);
   }
   static __device__ __forceinline__ void unpack(const raw& v, float (&f)[kVec]) {
     f[0] = __uint_as_float(v.a.x); f[1] = __uint_as_float(v.a.y);
@@ -370,11 +385,11 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) rr[i] = VA::template load<kLoadPolicy>(r_res, vec[i] * VA::kBytes);
-    // sum of partials in ascending rank order, then deepstack, then residual
+    // sum of the (scaled) partials in ascending rank order, then deepstack, then residual
 #pragma unroll
     for (int q = 0; q < TP; ++q)
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) VP::add(rp[q][i], z[i]);
+      for (int i = 0; i < VPT; ++i) VP::add_scaled(rp[q][i], a.pscale, z[i]);
     if (has_ds) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) VA::add(rd[i], z[i]);
@@ -400,7 +415,7 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
       for (int k = 0; k < G; ++k)
         if (k < g) {
 #pragma unroll
-          for (int i = 0; i < VPT; ++i) VP::add(rp[k][i], z[i]);
+          for (int i = 0; i < VPT; ++i) VP::add_scaled(rp[k][i], a.pscale, z[i]);
         }
     }
     if (has_ds) {
@@ -651,6 +666,44 @@ __global__ void __launch_bounds__(kMaxThreads) gather_kernel(const GArgs a) {
   }
 }
 
+// ------------------------------------------------------- FlashComm2 regroup
+
+struct FArgs {
+  const char* src[kMaxTp];  // rank q's [N][C]
+  char* dst[kMaxTp];        // rank r's [N/odp][odp*C]
+  int32_t odp;
+  int32_t seg_rows;         // N / G
+  int32_t dst_rows;         // N / odp
+  uint32_t piece;           // C * element size, bytes
+};
+
+// One workgroup per destination row: blockIdx.x = r * dst_rows + t.  Rank
+// r = g*odp + j, row t lies in its k-th segment (source segment j + k*odp,
+// row u of it); the row is the odp source rows of that token, side by side.
+template <int B>
+__global__ void __launch_bounds__(kMaxThreads) fc2_regroup_kernel(const FArgs a) {
+  const int64_t b = blockIdx.x;
+  const int r = static_cast<int>(b / a.dst_rows);
+  const int t = static_cast<int>(b - static_cast<int64_t>(r) * a.dst_rows);
+  const int g = r / a.odp, j = r - g * a.odp;
+  const int k = t / a.seg_rows, u = t - k * a.seg_rows;
+  const int64_t n = static_cast<int64_t>(j + k * a.odp) * a.seg_rows + u;  // source token
+  const uint32_t row_bytes = a.piece * static_cast<uint32_t>(a.odp);
+  const rsrc_t dst = row_rsrc(a.dst[r] + static_cast<int64_t>(t) * row_bytes, row_bytes);
+  for (uint32_t off = threadIdx.x * B; off < row_bytes; off += blockDim.x * B) {
+    const int i = static_cast<int>(off / a.piece);       // which rank of the ODP group
+    const uint32_t o = off - static_cast<uint32_t>(i) * a.piece;
+    const rsrc_t src = row_rsrc(a.src[g * a.odp + i] + n * a.piece, a.piece);
+    if constexpr (B == 16) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src, o, 0, kLoadPolicy),
+                                             dst, off, 0, kStorePolicy);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_raw_buffer_load_b32(src, o, 0, kLoadPolicy),
+                                            dst, off, 0, kStorePolicy);
+    }
+  }
+}
+
 // ------------------------------------------------------------ host checks
 
 thread_local char g_last_error[512] = "no error";
@@ -738,6 +791,9 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SP_ERR_SHAPE, "eps must be finite and >= 0");
   if (p->flags != 0 && p->flags != SP_FLAG_VALID_ROWS_ONLY)
     return fail(SP_ERR_UNSUPPORTED, "flags=%d unsupported", p->flags);
+  if (!(p->partial_scale == p->partial_scale) || p->partial_scale == __builtin_inff() ||
+      p->partial_scale == -__builtin_inff())
+    return fail(SP_ERR_SHAPE, "partial_scale must be finite");
   if (p->partial_stride != 0 && p->partial_stride < S * H)
     return fail(SP_ERR_SHAPE, "partial_stride=%lld is below S*H=%lld (partials would overlap)",
                 (long long)p->partial_stride, (long long)(S * H));
@@ -839,6 +895,7 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   ka.valid = static_cast<int32_t>(plan.valid);
   ka.tp = p->tp;
   ka.eps = eps;
+  ka.pscale = p->partial_scale == 0.0f ? 1.0f : p->partial_scale;
 
   const int om = quant_mode == SP_QUANT_STATIC_TENSOR   ? OM_FP8_STATIC
                  : quant_mode == SP_QUANT_DYNAMIC_TOKEN ? OM_FP8_DYN
@@ -921,6 +978,61 @@ int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
   hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(T)), dim3(static_cast<unsigned>(nt)), args,
                                    0, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(SP_ERR_HIP, "gather launch failed: %s", hipGetErrorString(err));
+  return SP_OK;
+}
+
+int sp_fc2_regroup(const sp_fc2_problem* f, const void* const* src, void* const* dst, void* stream) {
+  if (!f) return fail(SP_ERR_NULL, "fc2 descriptor is NULL");
+  const int G = f->global_tp, P = f->otp;
+  if (G < 2 || G > kMaxTp) return fail(SP_ERR_SHAPE, "global_tp=%d outside [2, %d]", G, kMaxTp);
+  if (P < 1 || P >= G || G % P != 0)
+    return fail(SP_ERR_SHAPE, "otp=%d must divide global_tp=%d and be smaller", P, G);
+  if (f->reserved != 0) return fail(SP_ERR_UNSUPPORTED, "reserved field must be 0");
+  const size_t e = elt_size(f->dtype);
+  if (e == 0) return fail(SP_ERR_DTYPE, "dtype=%d unsupported", f->dtype);
+  const int64_t N = f->tokens, C = f->cols;
+  if (N < 0 || N % G != 0 || N > INT32_MAX) return fail(SP_ERR_SHAPE, "tokens=%lld must be a multiple of %d", (long long)N, G);
+  if (C < 1 || (C * static_cast<int64_t>(e)) % 4 != 0 || C * static_cast<int64_t>(e) * (G / P) > (1ll << 30))
+    return fail(SP_ERR_SHAPE, "cols=%lld gives rows that are not a multiple of 4 bytes", (long long)C);
+  if (static_cast<int64_t>(P) * N > static_cast<int64_t>(UINT32_MAX))
+    return fail(SP_ERR_SHAPE, "otp * tokens exceeds the grid limit");
+  if (N == 0) return SP_OK;
+  if (!src || !dst) return fail(SP_ERR_NULL, "src and dst must be non-NULL");
+  const int odp = G / P;
+  const size_t piece = static_cast<size_t>(C) * e;
+  const int B = piece % 16 == 0 ? 16 : 4;
+  const uintptr_t amask = static_cast<uintptr_t>(B - 1);
+  const size_t src_n = static_cast<size_t>(N) * piece, dst_n = static_cast<size_t>(N / odp) * piece * odp;
+  FArgs fa;
+  memset(&fa, 0, sizeof fa);
+  for (int q = 0; q < G; ++q) {
+    if (!src[q] || !dst[q]) return fail(SP_ERR_NULL, "src[%d] or dst[%d] is NULL", q, q);
+    if ((reinterpret_cast<uintptr_t>(src[q]) | reinterpret_cast<uintptr_t>(dst[q])) & amask)
+      return fail(SP_ERR_ALIGN, "src[%d] / dst[%d] not %d-byte aligned", q, q, B);
+    fa.src[q] = static_cast<const char*>(src[q]);
+    fa.dst[q] = static_cast<char*>(dst[q]);
+  }
+  for (int r = 0; r < G; ++r)
+    for (int q = 0; q < G; ++q) {
+      if (overlap(dst[r], dst_n, src[q], src_n)) return fail(SP_ERR_SHAPE, "dst[%d] overlaps src[%d]", r, q);
+      if (q != r && overlap(dst[r], dst_n, dst[q], dst_n))
+        return fail(SP_ERR_SHAPE, "dst[%d] overlaps dst[%d]", r, q);
+    }
+  fa.odp = odp;
+  fa.seg_rows = static_cast<int32_t>(N / G);
+  fa.dst_rows = static_cast<int32_t>(N / odp);
+  fa.piece = static_cast<uint32_t>(piece);
+  int nt = static_cast<int>((piece * odp / B + 63) / 64 * 64);
+  nt = nt > kMaxThreads ? kMaxThreads : nt;
+  if (static_cast<int64_t>(P) * N * nt > static_cast<int64_t>(UINT32_MAX))
+    return fail(SP_ERR_SHAPE, "otp * tokens * %d threads exceeds the dispatch limit", nt);
+  void* args[] = {&fa};
+  const void* fn = B == 16 ? reinterpret_cast<const void*>(&fc2_regroup_kernel<16>)
+                           : reinterpret_cast<const void*>(&fc2_regroup_kernel<4>);
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(G) * (N / odp));
+  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(static_cast<unsigned>(nt)), args, 0,
+                                   static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SP_ERR_HIP, "fc2 regroup launch failed: %s", hipGetErrorString(err));
   return SP_OK;
 }
 

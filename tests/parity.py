@@ -67,7 +67,8 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
              in_place: bool = False, out_dtype: Optional[torch.dtype] = None,
              static_scale: Optional[float] = None, shard_deepstack: bool = False,
              inputs: Optional[dict] = None, base_seed: Optional[int] = None,
-             require_exact_frac: float = 0.99, fp4: bool = False) -> Result:
+             require_exact_frac: float = 0.99, fp4: bool = False,
+             partial_scale: float = 1.0) -> Result:
     S = w.shard_rows if S is None else S
     T = min(w.num_tokens, w.tp * S) if T is None else T
     kw = {} if base_seed is None else {"base_seed": base_seed}
@@ -102,7 +103,8 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
 
     sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], w.eps,
                              quant, x["deepstack"], out, scale_t, tp_rank=rank, num_tokens=T,
-                             residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if fp4 else None)
+                             residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if fp4 else None,
+                             partial_scale=partial_scale)
     torch.cuda.synchronize()
 
     # ---- canaries and untouched memory (byte-exact)
@@ -143,7 +145,8 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
         out_dtype=oracle.ORC_E2M1 if fp4 else {torch.bfloat16: oracle.ORC_BF16,
                                                 torch.float32: oracle.ORC_F32}.get(
             out_dtype, oracle.ORC_E4M3),
-        static_scale=static_scale if static_scale is not None else 1.0, rows=rows)
+        static_scale=static_scale if static_scale is not None else 1.0, rows=rows,
+        partial_scale=partial_scale)
 
     stats = {"rows": len(rows), "elements": len(rows) * H}
     valid = rows < v
@@ -164,7 +167,8 @@ def run_case(w: Workload, rank: int, *, dev, S: Optional[int] = None, T: Optiona
     z = ref["z"][valid]
     y = ref["y"][valid]
     P = _host_f64(h["partials"][:, vr, :])
-    A = np.abs(P).sum(0) + np.abs(_host_f64(h["residual"][roff + vr]))
+    c = abs(float(np.float32(partial_scale)))
+    A = c * np.abs(P).sum(0) + np.abs(_host_f64(h["residual"][roff + vr]))
     if h["deepstack"] is not None:
         doff = rank * S if h["deepstack"].shape[0] == tp * S and tp > 1 else 0
         A += np.abs(_host_f64(h["deepstack"][doff + vr]))

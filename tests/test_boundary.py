@@ -184,6 +184,54 @@ def test_gather_empty_is_a_no_op():
     assert _gather(S=0, T=0)[0] == sp.SP_OK
 
 
+def _fc2(G=4, otp=2, dtype=sp.SP_BF16, N=8, Cc=8, reserved=0, src=None, dst=None):
+    import ctypes as C
+    lib = sp.load()
+    f = sp.sp_fc2_problem(global_tp=G, otp=otp, dtype=dtype, reserved=reserved, tokens=N, cols=Cc)
+    src = src if src is not None else [BASE + q * GB for q in range(G)]
+    dst = dst if dst is not None else [BASE + (G + q) * GB for q in range(G)]
+    s = (C.c_void_p * len(src))(*src)
+    d = (C.c_void_p * len(dst))(*dst)
+    return lib.sp_fc2_regroup(C.byref(f), s, d, None), sp.sp_last_error()
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(G=1, otp=1, src=[BASE], dst=[BASE + GB]), sp.SP_ERR_SHAPE),
+    (dict(G=65, otp=5, src=[BASE] * 65, dst=[BASE + GB] * 65), sp.SP_ERR_SHAPE),
+    (dict(otp=4), sp.SP_ERR_SHAPE),                       # otp == G
+    (dict(otp=3), sp.SP_ERR_SHAPE),                       # does not divide G
+    (dict(otp=0), sp.SP_ERR_SHAPE),
+    (dict(reserved=1), sp.SP_ERR_UNSUPPORTED),
+    (dict(dtype=sp.SP_FP4_E2M1), sp.SP_ERR_DTYPE),
+    (dict(dtype=7), sp.SP_ERR_DTYPE),
+    (dict(N=10), sp.SP_ERR_SHAPE),                        # not a multiple of G
+    (dict(N=-4), sp.SP_ERR_SHAPE),
+    (dict(N=1 << 31), sp.SP_ERR_SHAPE),
+    (dict(Cc=3), sp.SP_ERR_SHAPE),                        # 6-byte rows
+    (dict(Cc=0), sp.SP_ERR_SHAPE),
+    (dict(G=64, otp=32, N=(1 << 31) - 64, Cc=1024, src=[BASE + q * GB for q in range(64)],
+          dst=[BASE + (64 + q) * GB for q in range(64)]), sp.SP_ERR_SHAPE),  # grid too large
+    (dict(G=2, otp=1, N=1 << 27, Cc=64, src=[BASE, BASE + 64 * GB],
+          dst=[BASE + 128 * GB, BASE + 192 * GB]), sp.SP_ERR_SHAPE),  # grid fits, work-items do not
+    (dict(src=[BASE, BASE + GB, 0, BASE + 3 * GB]), sp.SP_ERR_NULL),
+    (dict(dst=[BASE + 4 * GB, BASE + 5 * GB, BASE + 6 * GB, 0]), sp.SP_ERR_NULL),
+    (dict(src=[BASE, BASE + GB + 4, BASE + 2 * GB, BASE + 3 * GB]), sp.SP_ERR_ALIGN),  # 16-B rows
+    (dict(dst=[BASE + 4 * GB, BASE + 5 * GB, BASE + 2 * GB + 16, BASE + 7 * GB]), sp.SP_ERR_SHAPE),
+    (dict(dst=[BASE + 4 * GB, BASE + 5 * GB, BASE + 4 * GB + 16, BASE + 7 * GB]), sp.SP_ERR_SHAPE),
+])
+def test_fc2_regroup_rejects_invalid_problems(case, expect):
+    status, msg = _fc2(**case)
+    assert status == expect, msg
+    if case.get("N") == 1 << 27:
+        assert "dispatch" in msg
+
+
+def test_fc2_regroup_empty_is_a_no_op():
+    assert _fc2(N=0)[0] == sp.SP_OK
+    # 4-byte rows need only 4-byte alignment; N == 0 never touches the pointers
+    assert _fc2(N=0, Cc=2, src=[BASE + 4, BASE + GB, BASE + 2 * GB, BASE + 3 * GB])[0] == sp.SP_OK
+
+
 def test_null_descriptor():
     lib = sp.load()
     assert lib.sp_validate(None, None, None, None, None, 0.0, 0, None, None, None) == sp.SP_ERR_NULL

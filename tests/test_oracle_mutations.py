@@ -16,8 +16,9 @@ SRC = os.path.join(ROOT, "oracle", "sprms_oracle.c")
 
 MUTATIONS = {
     "drop_deepstack": ("if (deepstack) x += load(deepstack", "if (0) x += load(deepstack"),
-    "drop_last_partial": ("for (int64_t q = 0; q < tp; ++q) x +=",
-                          "for (int64_t q = 0; q < tp - 1; ++q) x +="),
+    "drop_last_partial": ("for (int64_t q = 0; q < tp; ++q)\n        x += p->partial_scale",
+                          "for (int64_t q = 0; q < tp - 1; ++q)\n        x += p->partial_scale"),
+    "partial_scale_ignored": ("x += p->partial_scale * load(", "x += load("),
     "eps_outside_sqrt": ("1.0 / sqrt(ss / (double)H + (double)eps)",
                          "1.0 / (sqrt(ss / (double)H) + (double)eps)"),
     "mean_over_h_minus_1": ("sqrt(ss / (double)H + ", "sqrt(ss / (double)(H - 1) + "),
@@ -42,6 +43,9 @@ MUTATIONS = {
     "mx_no_clamp_low": ("if (e < -127) e = -127;", "if (e < -150) e = -150;"),
     "e2m1_no_tie_to_even": ("if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {\n      best = c;\n      best_err = err;\n    }\n  }\n  return (uint8_t)(best | (signbit(x) ? 0x8 : 0x0));",
                             "if (err <= best_err) {\n      best = c;\n      best_err = err;\n    }\n  }\n  return (uint8_t)(best | (signbit(x) ? 0x8 : 0x0));"),
+    "fc2_contiguous_segments": ("ids[j * otp + k] = j + k * odp;", "ids[j * otp + k] = j * otp + k;"),
+    "fc2_senders_reversed": ("const char* from = (const char*)src[g * odp + i]",
+                             "const char* from = (const char*)src[g * odp + (odp - 1 - i)]"),
     "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
                              "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
     "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",

@@ -137,12 +137,13 @@ def test_shard_geometry_rejects_bad_layouts(args):
 
 
 def _run(partials, residual, weight, bias=None, eps=0.0, quant=NONE, deepstack=None, tp_rank=0,
-         num_tokens=None, out_dtype=oracle.ORC_F32, static_scale=1.0, rows=None):
+         num_tokens=None, out_dtype=oracle.ORC_F32, static_scale=1.0, rows=None, partial_scale=1.0):
     tp, S, H = np.asarray(partials).shape
     return oracle.reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant, deepstack,
                                      tp_rank=tp_rank,
                                      num_tokens=tp * S if num_tokens is None else num_tokens,
-                                     out_dtype=out_dtype, static_scale=static_scale, rows=rows)
+                                     out_dtype=out_dtype, static_scale=static_scale, rows=rows,
+                                     partial_scale=partial_scale)
 
 
 def test_closed_form_rmsnorm_rows():
@@ -589,3 +590,73 @@ def test_mx_codes_decode_within_half_a_step():
                 tmax = 6.0
             d = dec[32 * b:32 * b + 32]
             assert (np.abs(d - np.clip(t, -tmax, tmax)) <= step / 2 + 1e-12).all()
+
+
+
+def test_partials_scaled_before_the_sum():
+    # [PR18671] §5.3: the o_proj output is multiplied by a factor before the
+    # reduction.  Partials (4, 0, 0, 0) and (-2, 2, 0, 0) scaled by 1/2 sum to
+    # (1, 1, 0, 0); residual (1, -1, 0, 0) gives z = (2, 0, 0, 0) -> y = (2w0, 0, 0, 0).
+    w = f32([1.5, 2.0, -1.0, 0.5])
+    P = f32([[[4, 0, 0, 0]], [[-2, 2, 0, 0]]])
+    r = _run(P, f32([[1, -1, 0, 0]]), w, partial_scale=0.5)
+    np.testing.assert_array_equal(r["residual_out"], [[2, 0, 0, 0]])
+    np.testing.assert_array_equal(r["out"], [[3.0, 0, 0, 0]])
+    # scaling every partial by c equals feeding c-scaled partials
+    rng = np.random.default_rng(12)
+    P = rng.normal(0, 0.5, (3, 4, 16)).astype(np.float32)
+    R = rng.normal(0, 1, (4, 16)).astype(np.float32)
+    a = _run(P, R, np.ones(16, np.float32), partial_scale=0.25, eps=1e-6)
+    c = _run(P * np.float32(0.25), R, np.ones(16, np.float32), eps=1e-6)
+    np.testing.assert_array_equal(a["z"], c["z"])
+
+
+# ------------------------------------------------- FlashComm2 regrouping
+
+
+def test_fc2_regroup_matches_worked_example():
+    with open(os.path.join(GOLDEN, "fc2_regroup_example.json")) as f:
+        g = json.load(f)
+    G, otp = g["global_tp"], g["otp"]
+    assert oracle.fc2_batch_ids(G, otp) == g["batch_ids"]
+    N, Cc = 8, 3                      # 4 segments of 2 tokens, 3 feature columns per rank
+    seg = N // G
+    # value = 100*token + 10*rank + column: every element says where it came from
+    srcs = [np.array([[100 * n + 10 * q + c for c in range(Cc)] for n in range(N)], np.float32)
+            for q in range(G)]
+    dsts = oracle.fc2_regroup(srcs, otp)
+    letters = g["features"]
+    for r, blocks in g["rank_rows"].items():
+        d = dsts[int(r)]
+        assert d.shape == (N // (G // otp), (G // otp) * Cc)
+        for b, (tok, feats) in enumerate(blocks):
+            segment = int(tok[1:])
+            for u in range(seg):
+                row = d[b * seg + u]
+                n = segment * seg + u
+                want = [100 * n + 10 * letters.index(ch) + c for ch in feats for c in range(Cc)]
+                np.testing.assert_array_equal(row, want)
+
+
+@pytest.mark.parametrize("G,otp", [(8, 2), (8, 4), (16, 4), (6, 3)])
+def test_fc2_regroup_then_otp_reduce_gives_sequence_parallel_layout(G, otp):
+    # [SP/FC] §4.5-4.6: the OTP group of rank r (same position j) computes
+    # o_proj on the same tokens with different feature columns; its
+    # reduce-scatter hands rank r token segment r -- the same rows and the
+    # same sums as the global-TP reduce-scatter.  Integer data: exact.
+    rng = np.random.default_rng(G * 10 + otp)
+    N, Cc, Hout = 4 * G, 2, 5
+    X = rng.integers(-3, 4, (N, G * Cc)).astype(np.float64)       # all features of all tokens
+    W = rng.integers(-3, 4, (G * Cc, Hout)).astype(np.float64)    # o_proj weight
+    srcs = [np.ascontiguousarray(X[:, q * Cc:(q + 1) * Cc]) for q in range(G)]
+    dsts = oracle.fc2_regroup(srcs, otp)
+    odp, seg = G // otp, N // G
+    tp_sum = X @ W                                                 # global-TP all-reduce
+    for r in range(G):
+        gidx, j = divmod(r, odp)
+        total = np.zeros((seg, Hout))
+        for g2 in range(otp):                                      # OTP group of r
+            r2 = g2 * odp + j
+            part = dsts[r2] @ W[g2 * odp * Cc:(g2 + 1) * odp * Cc]  # its o_proj partial
+            total += part[gidx * seg:(gidx + 1) * seg]             # rows of segment r
+        np.testing.assert_array_equal(total, tp_sum[r * seg:(r + 1) * seg])
