@@ -20,6 +20,7 @@ from .oracle import (  # noqa: F401
     bf16_from_double_array,
     bf16_to_double,
     build,
+    dsacp_heads_to_tokens,
     e2m1_from_double,
     e2m1_from_double_array,
     e2m1_to_double,

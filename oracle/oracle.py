@@ -87,6 +87,8 @@ def _load():
     lib.orc_fc2_batch_ids.restype = C.c_int
     lib.orc_fc2_regroup.argtypes = [i32, i32, i64, i64, i32, C.POINTER(vp), C.POINTER(vp)]
     lib.orc_fc2_regroup.restype = C.c_int
+    lib.orc_dsacp_heads_to_tokens.argtypes = [i32, i64, i64, C.POINTER(vp), C.POINTER(vp)]
+    lib.orc_dsacp_heads_to_tokens.restype = C.c_int
     lib.orc_e2m1_from_double.argtypes = [C.c_double]
     lib.orc_e2m1_from_double.restype = C.c_uint8
     lib.orc_e2m1_to_double.argtypes = [C.c_uint8]
@@ -277,3 +279,23 @@ def fc2_regroup(srcs, otp: int):
     if rc != 0:
         raise OracleError(f"orc_fc2_regroup failed: {rc}")
     return dsts
+
+
+def dsacp_heads_to_tokens(attn):
+    """DSA-CP o_proj input exchange: tp host arrays [S, tp*D] (rank p's local
+    tokens, every rank's heads) -> tp arrays [tp*S, D] (every token, rank q's
+    heads)."""
+    lib = _load()
+    attn = [np.ascontiguousarray(a) for a in attn]
+    tp = len(attn)
+    S, W = attn[0].shape
+    if W % tp:
+        raise OracleError("row width is not a multiple of tp")
+    D = W // tp
+    outs = [np.zeros((tp * S, D), dtype=attn[0].dtype) for _ in range(tp)]
+    ap = (C.c_void_p * tp)(*[a.ctypes.data for a in attn])
+    op = (C.c_void_p * tp)(*[a.ctypes.data for a in outs])
+    rc = lib.orc_dsacp_heads_to_tokens(tp, S, D * attn[0].dtype.itemsize, ap, op)
+    if rc != 0:
+        raise OracleError(f"orc_dsacp_heads_to_tokens failed: {rc}")
+    return outs

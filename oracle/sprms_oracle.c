@@ -467,3 +467,37 @@ int orc_fc2_regroup(int32_t G, int32_t otp, int64_t N, int64_t C, int32_t elt,
     }
   return ORC_OK;
 }
+
+/* ----------------------------------------- DSA-CP o_proj all-to-all (path B) */
+
+/* [PR18671] §5.3, path B, the two steps before o_proj written out.  Rank p
+ * holds attn[p], its S local tokens with every rank's heads, [S][tp*D].
+ * Step 1 (view [S, tp, D], move the tp axis first, flatten): the send
+ * buffer of rank p is [tp*S][D] with row q*S + s = columns [q*D, (q+1)*D)
+ * of token s.  Step 2 (all_to_all_single over the tp group): the send
+ * buffer is cut into tp equal chunks of S rows, chunk q goes to rank q, and
+ * rank q stacks what it receives in sender order, so out[q] is [tp*S][D]
+ * with row p*S + s from chunk q of rank p: every token of the group, rank
+ * q's heads only.  piece = D * element bytes. */
+int orc_dsacp_heads_to_tokens(int32_t tp, int64_t S, int64_t piece, const void* const* attn,
+                              void* const* out) {
+  if (tp < 1 || S < 0 || piece < 1) return ORC_ERR_SHAPE;
+  if (S > 0 && (!attn || !out)) return ORC_ERR_NULL;
+  if (S == 0) return ORC_OK;
+  const size_t chunk = (size_t)S * (size_t)piece; /* S rows of one head block */
+  char* send = (char*)malloc((size_t)tp * chunk);
+  if (!send) return ORC_ERR_SHAPE;
+  for (int p = 0; p < tp; ++p) {
+    /* step 1 on rank p */
+    for (int q = 0; q < tp; ++q)
+      for (int64_t s = 0; s < S; ++s)
+        memcpy(send + (size_t)q * chunk + (size_t)s * (size_t)piece,
+               (const char*)attn[p] + ((size_t)s * (size_t)tp + (size_t)q) * (size_t)piece,
+               (size_t)piece);
+    /* step 2: rank p's chunk q lands in rank q's buffer at chunk position p */
+    for (int q = 0; q < tp; ++q)
+      memcpy((char*)out[q] + (size_t)p * chunk, send + (size_t)q * chunk, chunk);
+  }
+  free(send);
+  return ORC_OK;
+}

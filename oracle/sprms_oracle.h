@@ -102,6 +102,11 @@ int orc_fc2_batch_ids(int32_t G, int32_t otp, int32_t* ids);
 int orc_fc2_regroup(int32_t G, int32_t otp, int64_t N, int64_t C, int32_t elt,
                     const void* const* src, void* const* dst);
 
+/* DSA-CP o_proj input exchange, [PR18671] §5.3 path B: attn[p] [S][tp*D] ->
+ * out[q] [tp*S][D], row p*S + s = attn[p][s][q*D .. (q+1)*D). */
+int orc_dsacp_heads_to_tokens(int32_t tp, int64_t S, int64_t piece, const void* const* attn,
+                              void* const* out);
+
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
 double orc_bf16_to_double(uint16_t bits);

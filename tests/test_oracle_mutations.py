@@ -46,6 +46,10 @@ MUTATIONS = {
     "fc2_contiguous_segments": ("ids[j * otp + k] = j + k * odp;", "ids[j * otp + k] = j * otp + k;"),
     "fc2_senders_reversed": ("const char* from = (const char*)src[g * odp + i]",
                              "const char* from = (const char*)src[g * odp + (odp - 1 - i)]"),
+    "dsacp_chunk_of_sender": ("memcpy((char*)out[q] + (size_t)p * chunk, send + (size_t)q * chunk, chunk);",
+                              "memcpy((char*)out[q] + (size_t)p * chunk, send + (size_t)p * chunk, chunk);"),
+    "dsacp_head_major_view": ("((size_t)s * (size_t)tp + (size_t)q) * (size_t)piece",
+                              "((size_t)q * (size_t)S + (size_t)s) * (size_t)piece"),
     "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
                              "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
     "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",

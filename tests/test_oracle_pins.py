@@ -660,3 +660,38 @@ def test_fc2_regroup_then_otp_reduce_gives_sequence_parallel_layout(G, otp):
             part = dsts[r2] @ W[g2 * odp * Cc:(g2 + 1) * odp * Cc]  # its o_proj partial
             total += part[gidx * seg:(gidx + 1) * seg]             # rows of segment r
         np.testing.assert_array_equal(total, tp_sum[r * seg:(r + 1) * seg])
+
+
+# ------------------------------------------- DSA-CP o_proj exchange (path B)
+
+
+@pytest.mark.parametrize("tp,S,D", [(2, 3, 2), (4, 5, 3), (8, 2, 4), (16, 3, 1)])
+def test_dsacp_path_b_equals_path_a(tp, S, D):
+    # [PR18671] §5.3: path A runs o_proj with the full weight on the rank's
+    # own tokens and all heads; path B exchanges heads for tokens, runs the
+    # row-parallel o_proj on the rank's heads, scales, reduce-scatters.  Both
+    # must hand every rank the same output rows (integers: exact).
+    rng = np.random.default_rng(tp * 100 + S)
+    Hout = 7
+    attn = [rng.integers(-3, 4, (S, tp * D)).astype(np.float64) for _ in range(tp)]
+    W = rng.integers(-3, 4, (tp * D, Hout)).astype(np.float64)
+    c = 0.5                                             # a power of two keeps it exact
+    recv = oracle.dsacp_heads_to_tokens(attn)
+    for q in range(tp):
+        assert recv[q].shape == (tp * S, D)
+    proj = [c * (recv[q] @ W[q * D:(q + 1) * D]) for q in range(tp)]   # [tp*S, Hout] each
+    for p in range(tp):
+        path_b = sum(proj[q][p * S:(p + 1) * S] for q in range(tp))     # RS: rank p's rows
+        path_a = c * (attn[p] @ W)
+        np.testing.assert_array_equal(path_b, path_a)
+
+
+@pytest.mark.parametrize("tp,S,D", [(2, 4, 8), (4, 3, 5), (8, 1, 2)])
+def test_dsacp_exchange_is_undone_by_the_plain_all_to_all(tp, S, D):
+    # the FC2 regroup with otp = 1 (one ODP group: every rank takes its own
+    # token segment with all features) is the inverse permutation
+    rng = np.random.default_rng(tp + S + D)
+    attn = [rng.integers(0, 1 << 16, (S, tp * D)).astype(np.uint16) for _ in range(tp)]
+    back = oracle.fc2_regroup(oracle.dsacp_heads_to_tokens(attn), otp=1)
+    for p in range(tp):
+        np.testing.assert_array_equal(back[p], attn[p])
