@@ -34,15 +34,19 @@ from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK, 
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + shard tokens/s for fused reduce-add-RMSNorm"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
-KERNEL_SRC = os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc", "sprms.hip")
+# sources of the fused kernel (the layout kernels live in csrc/layout.hip)
+KERNEL_SRCS = [os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc", f) for f in ("sprms.hip", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
 QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3",
                4: "block-scaled (32-element E8M0 scales)"}
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

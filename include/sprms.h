@@ -190,7 +190,9 @@ typedef struct {
   int32_t global_tp;  /* G, ranks of the tensor-parallel group, 2 <= G <= 64 */
   int32_t otp;        /* ranks that compute o_proj together, 1 <= otp < G, G % otp == 0 */
   int32_t dtype;      /* element type: SP_F32 | SP_BF16 | SP_FP8_E4M3 */
-  int32_t reserved;   /* 0 */
+  int32_t rank;       /* -1: write every rank's dst (one GPU holding the whole group);
+                         0 <= rank < G: write dst[rank] only (a rank's own call on a node,
+                         the other dst entries are ignored and may be NULL) */
   int64_t tokens;     /* N, N % G == 0, 0 <= N < 2^31 */
   int64_t cols;       /* C = H / G, feature columns held by each rank, C * elt % 4 == 0 */
 } sp_fc2_problem;
@@ -211,14 +213,53 @@ typedef struct {
  *        columns of every token); on a node, peer-mapped buffers
  *   dst  host array of G device pointers, rank r's [N/odp][odp*C] output
  *
- * Pointers 16-byte aligned (4-byte when C * elt % 16 != 0); a dst must not
- * overlap any src or another dst.  Bytes are copied unchanged, one workgroup
- * per destination row, so otp * N times the workgroup size (up to 1024) must
- * stay below 2^32.  N == 0 enqueues nothing.  Same error convention as
- * sp_reduce_add_rmsnorm.
+ * Pointers 16-byte aligned (4-byte when C * elt % 16 != 0); a written dst
+ * must not overlap any src or another written dst.  Bytes are copied
+ * unchanged, one workgroup per destination row, so the rows written times
+ * the workgroup size (up to 1024) must stay below 2^32.  N == 0 enqueues
+ * nothing.  Same error convention as sp_reduce_add_rmsnorm.
  */
 int sp_fc2_regroup(const sp_fc2_problem* f, const void* const* src, void* const* dst,
                    void* stream);
+
+/* Problem descriptor of sp_dsacp_heads_to_tokens (host memory, read during the call only). */
+typedef struct {
+  int32_t tp;          /* ranks of the tensor-parallel group, 1 <= tp <= 64 */
+  int32_t dtype;       /* element type: SP_F32 | SP_BF16 | SP_FP8_E4M3 */
+  int32_t rank;        /* -1: every rank's output; 0 <= rank < tp: out[rank] only (the
+                          other out entries are ignored and may be NULL) */
+  int32_t reserved;    /* 0 */
+  int64_t shard_rows;  /* S, tokens of each rank's (padded) shard, 0 <= tp*S < 2^31 */
+  int64_t head_cols;   /* D, columns of one rank's heads (heads per rank x value head
+                          dim), D * elt % 4 == 0 */
+} sp_dsacp_problem;
+
+/*
+ * sp_dsacp_heads_to_tokens -- the exchange in front of o_proj on DSA-CP's
+ * path B (vllm-ascend PR #18671 walkthrough, §5.3): under sequence
+ * parallelism rank p's attention output holds its S local tokens with every
+ * rank's heads, [S][tp*D]; o_proj is row-parallel over the heads, so each
+ * rank needs every token with its own heads.  The page's view [S, tp, D],
+ * permute(1, 0, 2) and all_to_all_single over the tp group amount to
+ *
+ *   out[q][p*S + s][d] = attn[p][s][q*D + d]
+ *
+ * after which o_proj (row-parallel, unreduced), the output scale and one
+ * reduce-scatter hand rank p its S rows again: the fused call of this
+ * library with partial_scale = the output scale.
+ *
+ *   f      problem descriptor (host)
+ *   attn   host array of tp device pointers, rank p's [S][tp*D]; on a node,
+ *          peer-mapped buffers
+ *   out    host array of tp device pointers, rank q's [tp*S][D]
+ *
+ * Pointers 16-byte aligned (4-byte when D * elt % 16 != 0); a written out
+ * must not overlap any attn or another written out.  Bytes are copied
+ * unchanged.  S == 0 enqueues nothing.  Same error convention as
+ * sp_reduce_add_rmsnorm.
+ */
+int sp_dsacp_heads_to_tokens(const sp_dsacp_problem* f, const void* const* attn,
+                             void* const* out, void* stream);
 
 /*
  * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.

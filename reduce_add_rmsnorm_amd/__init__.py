@@ -30,7 +30,7 @@ SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED
     0, -1, -2, -3, -4, -5, -6)
 
 EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_fc2_regroup",
-            "sp_shard_geometry", "sp_error_string", "sp_last_error")
+            "sp_dsacp_heads_to_tokens", "sp_shard_geometry", "sp_error_string", "sp_last_error")
 SP_FLAG_VALID_ROWS_ONLY = 1
 
 
@@ -75,9 +75,20 @@ class sp_fc2_problem(C.Structure):
         ("global_tp", C.c_int32),
         ("otp", C.c_int32),
         ("dtype", C.c_int32),
-        ("reserved", C.c_int32),
+        ("rank", C.c_int32),
         ("tokens", C.c_int64),
         ("cols", C.c_int64),
+    ]
+
+
+class sp_dsacp_problem(C.Structure):
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("dtype", C.c_int32),
+        ("rank", C.c_int32),
+        ("reserved", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("head_cols", C.c_int64),
     ]
 
 
@@ -107,6 +118,9 @@ def load(build_if_missing: bool = False):
     lib.sp_all_gather_unpad.restype = C.c_int
     lib.sp_fc2_regroup.argtypes = [C.POINTER(sp_fc2_problem), C.POINTER(vp), C.POINTER(vp), vp]
     lib.sp_fc2_regroup.restype = C.c_int
+    lib.sp_dsacp_heads_to_tokens.argtypes = [C.POINTER(sp_dsacp_problem), C.POINTER(vp),
+                                             C.POINTER(vp), vp]
+    lib.sp_dsacp_heads_to_tokens.restype = C.c_int
     lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
                                       C.POINTER(i64)]
     lib.sp_shard_geometry.restype = C.c_int
@@ -139,6 +153,28 @@ def _addr(x) -> Optional[int]:
     if not x.is_contiguous():
         raise ValueError("tensors passed to libsprms must be contiguous")
     return x.data_ptr()
+
+
+def _same_device(*tensors):
+    """Every tensor given (None entries and lists of tensors allowed) is on the
+    same GPU; returns that device.  A host tensor would hand the kernels a
+    host address."""
+    flat = []
+    for t in tensors:
+        if isinstance(t, (list, tuple)):
+            flat.extend(x for x in t if x is not None)
+        elif t is not None:
+            flat.append(t)
+    flat = [t for t in flat if not isinstance(t, int)]
+    if not flat:
+        raise ValueError("no tensor arguments")
+    dev = flat[0].device
+    for t in flat:
+        if not t.is_cuda:
+            raise ValueError("libsprms takes device tensors only (got a host tensor)")
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+    return dev
 
 
 def _check(status: int):
@@ -199,8 +235,7 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
     current stream on partials' device).
     """
     lib = load()
-    if not partials.is_cuda:
-        raise ValueError("partials must be a device tensor")
+    _same_device(partials, residual, weight, bias, deepstack, out, out_scale, residual_out)
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out,
                         valid_rows_only=valid_rows_only, out_dtype=out_dtype,
@@ -221,8 +256,7 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
     no-argument callable that enqueues the call again (for timing loops).
     The tensors must stay alive and in place while the callable is used."""
     lib = load()
-    if not partials.is_cuda:
-        raise ValueError("partials must be a device tensor")
+    _same_device(partials, residual, weight, bias, deepstack, out, out_scale, residual_out)
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out, out_dtype=out_dtype)
     if stream is None:
@@ -251,8 +285,7 @@ def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int
     for t in shards:
         if t.shape != (S, W) or t.dtype != shards[0].dtype:
             raise ValueError("all shards must share shape and dtype")
-    if not shards[0].is_cuda:
-        raise ValueError("shards must be device tensors")
+    _same_device(shards, shard_scales, out, out_scale)
     dt = _sp_dtype(shards[0].dtype) if dtype is None else dtype
     H = 2 * W if dt == SP_FP4_E2M1 else W
     srow = 0 if shard_scales is None else shard_scales[0].nbytes // max(S, 1)
@@ -269,9 +302,16 @@ def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int
         _check(lib.sp_all_gather_unpad(C.byref(g), src, ssrc, _addr(out), _addr(out_scale), handle))
 
 
-def sp_fc2_regroup(srcs, dsts, *, otp: int, stream=None) -> None:
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def sp_fc2_regroup(srcs, dsts, *, otp: int, rank: int = -1, stream=None) -> None:
     """FlashComm2 o_proj input regrouping of G ranks: srcs[q] [N, C] ->
-    dsts[r] [N/odp, odp*C], odp = G/otp; see include/sprms.h."""
+    dsts[r] [N/odp, odp*C], odp = G/otp; with rank >= 0 only dsts[rank] is
+    written (the others may be None).  See include/sprms.h."""
     lib = load()
     G = len(srcs)
     N, Cc = srcs[0].shape
@@ -280,15 +320,36 @@ def sp_fc2_regroup(srcs, dsts, *, otp: int, stream=None) -> None:
             raise ValueError("all sources must share shape and dtype")
     if len(dsts) != G:
         raise ValueError("one destination per rank")
-    f = sp_fc2_problem(global_tp=G, otp=otp, dtype=_sp_dtype(srcs[0].dtype), reserved=0,
+    _same_device(srcs, dsts)
+    f = sp_fc2_problem(global_tp=G, otp=otp, dtype=_sp_dtype(srcs[0].dtype), rank=rank,
                        tokens=N, cols=Cc)
     src = (C.c_void_p * G)(*[_addr(t) for t in srcs])
     dst = (C.c_void_p * G)(*[_addr(t) for t in dsts])
     with torch.cuda.device(srcs[0].device):
-        if stream is None:
-            stream = torch.cuda.current_stream(srcs[0].device)
-        handle = stream if isinstance(stream, int) else stream.cuda_stream
-        _check(lib.sp_fc2_regroup(C.byref(f), src, dst, handle))
+        _check(lib.sp_fc2_regroup(C.byref(f), src, dst, _stream_handle(srcs[0].device, stream)))
+
+
+def sp_dsacp_heads_to_tokens(attn, outs, *, rank: int = -1, stream=None) -> None:
+    """DSA-CP o_proj input exchange of tp ranks: attn[p] [S, tp*D] (local
+    tokens, every rank's heads) -> outs[q] [tp*S, D] (every token, rank q's
+    heads); with rank >= 0 only outs[rank] is written (the others may be
+    None).  See include/sprms.h."""
+    lib = load()
+    tp = len(attn)
+    S, W = attn[0].shape
+    for t in attn:
+        if t.shape != (S, W) or t.dtype != attn[0].dtype:
+            raise ValueError("all inputs must share shape and dtype")
+    if W % tp or len(outs) != tp:
+        raise ValueError("row width must be tp*D and there must be one output per rank")
+    _same_device(attn, outs)
+    f = sp_dsacp_problem(tp=tp, dtype=_sp_dtype(attn[0].dtype), rank=rank, reserved=0,
+                         shard_rows=S, head_cols=W // tp)
+    src = (C.c_void_p * tp)(*[_addr(t) for t in attn])
+    dst = (C.c_void_p * tp)(*[_addr(t) for t in outs])
+    with torch.cuda.device(attn[0].device):
+        _check(lib.sp_dsacp_heads_to_tokens(C.byref(f), src, dst,
+                                            _stream_handle(attn[0].device, stream)))
 
 
 def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,

@@ -11,7 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "sprms.hip")
+# the fused shard kernel and the layout kernels (gather, regroupings)
+SRCS = [os.path.join(PKG, "csrc", "sprms.hip"), os.path.join(PKG, "csrc", "layout.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsprms.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,9 +26,9 @@ HIPCC_FLAGS = [
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile csrc/sprms.hip into libsprms.so (always recompiles)."""
+    """Compile csrc/*.hip into libsprms.so (always recompiles)."""
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [HIPCC, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,8 +3,9 @@
 // shard, written for MI355X (gfx950, CDNA4).
 //
 // What is computed is stated in include/sprms.h, with the passages of the
-// pages that define it.  This file is the implementation: host-side
-// validation and dispatch behind the C ABI, and one family of kernels.
+// pages that define it.  This file is the fused kernel family, its host-side
+// validation and dispatch behind the C ABI, and the library's error channel;
+// the layout kernels (gather, regroupings) are in layout.hip.
 //
 // Kernel design (HBM-bandwidth bound: about one flop per byte and no dense
 // contraction, so no MFMA):
@@ -39,18 +40,35 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "common.h"
 #include "sprms.h"
 
+namespace sprms {
+
 namespace {
+thread_local char g_last_error[512] = "no error";
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace sprms
+
+namespace {
+
+using namespace sprms;
 
 constexpr int kVec = 8;  // elements per thread-vector
 // Workgroup size bounds: one 8-element vector per thread allows a
 // 1024-thread workgroup (rows of up to 8192 elements); more vectors per
 // thread hold more registers and are limited to 512 threads.
-constexpr int kMaxThreads = 1024;
 constexpr int kMaxThreadsMultiVec = 512;
 constexpr int kMaxWaves = kMaxThreads / 64;
-constexpr int kMaxHidden = 32768;
 
 template <int VPT>
 constexpr int max_threads() {
@@ -77,41 +95,6 @@ struct KArgs {
   float eps;
   float pscale;           // factor applied to every partial before the sum
 };
-
-// ------------------------------------------------------------ element I/O
-//
-// All row data moves through buffer instructions.  A resource descriptor
-// covers exactly one row of one tensor (its base is uniform per workgroup,
-// so it lives in scalar registers); the per-lane operand is a 32-bit byte
-// offset inside the row.
-
-// Cache policy of the streamed (read-once / write-once) row data, as the
-// buffer instruction's cache-policy bits on gfx950: bit 0 sc0, bit 1 nt,
-// bit 4 sc1.  Gain and bias are re-read by every row and use policy 0.
-#ifndef SPRMS_STREAM_LOAD_POLICY
-#define SPRMS_STREAM_LOAD_POLICY 2
-#endif
-#ifndef SPRMS_STREAM_STORE_POLICY
-#define SPRMS_STREAM_STORE_POLICY 2
-#endif
-constexpr int kLoadPolicy = SPRMS_STREAM_LOAD_POLICY;
-constexpr int kStorePolicy = SPRMS_STREAM_STORE_POLICY;
-constexpr int kCachedPolicy = 0;
-
-// word 3 of a gfx9-family buffer descriptor: 32-bit data format, raw
-// (stride 0) addressing with the range check against num_records
-constexpr int kRsrcWord3 = 0x00020000;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-
-__device__ __forceinline__ rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           kRsrcWord3);
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
@@ -623,120 +606,13 @@ void launch_shape(int nvec, int* vpt, int* nt) {
   *nt = n;
 }
 
-// ------------------------------------------------------------ all-gather
-
-constexpr int kMaxTp = 64;
-
-struct GArgs {
-  const char* src[kMaxTp];     // shard q's [S][H] output
-  const char* ssrc[kMaxTp];    // shard q's [S][scale_row_bytes] scales (or all null)
-  char* out;                   // [T][H]
-  char* out_scale;             // [T][scale_row_bytes] or null
-  int64_t S;
-  uint32_t row_bytes;          // bytes of one output row
-  uint32_t scale_row_bytes;    // 0 when there are no scales
-};
-
-// One workgroup per gathered row t: shard q = t / S, row s = t - q*S, copied
-// unchanged with non-temporal 16-byte (or 8-byte) accesses.  The source and
-// destination descriptors cover exactly one row.
-template <int B>
-__global__ void __launch_bounds__(kMaxThreads) gather_kernel(const GArgs a) {
-  const int64_t t = blockIdx.x;
-  const int q = static_cast<int>(t / a.S);
-  const int64_t s = t - static_cast<int64_t>(q) * a.S;
-  const rsrc_t src = row_rsrc(a.src[q] + s * a.row_bytes, a.row_bytes);
-  const rsrc_t dst = row_rsrc(a.out + t * a.row_bytes, a.row_bytes);
-  for (uint32_t off = threadIdx.x * B; off < a.row_bytes; off += blockDim.x * B) {
-    if constexpr (B == 16) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, kLoadPolicy);
-      __builtin_amdgcn_raw_buffer_store_b128(v, dst, off, 0, kStorePolicy);
-    } else {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(src, off, 0, kLoadPolicy);
-      __builtin_amdgcn_raw_buffer_store_b64(v, dst, off, 0, kStorePolicy);
-    }
-  }
-  if (a.scale_row_bytes) {
-    const rsrc_t ssrc = row_rsrc(a.ssrc[q] + s * a.scale_row_bytes, a.scale_row_bytes);
-    const rsrc_t sdst = row_rsrc(a.out_scale + t * a.scale_row_bytes, a.scale_row_bytes);
-    for (uint32_t off = threadIdx.x; off < a.scale_row_bytes; off += blockDim.x) {
-      const uint8_t v = __builtin_amdgcn_raw_buffer_load_b8(ssrc, off, 0, kLoadPolicy);
-      __builtin_amdgcn_raw_buffer_store_b8(v, sdst, off, 0, kStorePolicy);
-    }
-  }
-}
-
-// ------------------------------------------------------- FlashComm2 regroup
-
-struct FArgs {
-  const char* src[kMaxTp];  // rank q's [N][C]
-  char* dst[kMaxTp];        // rank r's [N/odp][odp*C]
-  int32_t odp;
-  int32_t seg_rows;         // N / G
-  int32_t dst_rows;         // N / odp
-  uint32_t piece;           // C * element size, bytes
-};
-
-// One workgroup per destination row: blockIdx.x = r * dst_rows + t.  Rank
-// r = g*odp + j, row t lies in its k-th segment (source segment j + k*odp,
-// row u of it); the row is the odp source rows of that token, side by side.
-template <int B>
-__global__ void __launch_bounds__(kMaxThreads) fc2_regroup_kernel(const FArgs a) {
-  const int64_t b = blockIdx.x;
-  const int r = static_cast<int>(b / a.dst_rows);
-  const int t = static_cast<int>(b - static_cast<int64_t>(r) * a.dst_rows);
-  const int g = r / a.odp, j = r - g * a.odp;
-  const int k = t / a.seg_rows, u = t - k * a.seg_rows;
-  const int64_t n = static_cast<int64_t>(j + k * a.odp) * a.seg_rows + u;  // source token
-  const uint32_t row_bytes = a.piece * static_cast<uint32_t>(a.odp);
-  const rsrc_t dst = row_rsrc(a.dst[r] + static_cast<int64_t>(t) * row_bytes, row_bytes);
-  for (uint32_t off = threadIdx.x * B; off < row_bytes; off += blockDim.x * B) {
-    const int i = static_cast<int>(off / a.piece);       // which rank of the ODP group
-    const uint32_t o = off - static_cast<uint32_t>(i) * a.piece;
-    const rsrc_t src = row_rsrc(a.src[g * a.odp + i] + n * a.piece, a.piece);
-    if constexpr (B == 16) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src, o, 0, kLoadPolicy),
-                                             dst, off, 0, kStorePolicy);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_raw_buffer_load_b32(src, o, 0, kLoadPolicy),
-                                            dst, off, 0, kStorePolicy);
-    }
-  }
-}
-
 // ------------------------------------------------------------ host checks
-
-thread_local char g_last_error[512] = "no error";
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
-  va_end(ap);
-  return code;
-}
-
-size_t elt_size(int dt) { return dt == SP_F32 ? 4 : dt == SP_BF16 ? 2 : dt == SP_FP8_E4M3 ? 1 : 0; }
-
-// bytes of one row of H elements (e2m1: two per byte); 0 for an unknown type
-size_t row_bytes_of(int dt, int64_t H) {
-  if (dt == SP_FP4_E2M1) return static_cast<size_t>(H) / 2;
-  return static_cast<size_t>(H) * elt_size(dt);
-}
 
 // bytes of out_scale per row, per quant mode (static: one f32 for the tensor)
 size_t scale_row_bytes_of(int quant_mode, int64_t H) {
   if (quant_mode == SP_QUANT_DYNAMIC_TOKEN) return 4;
   if (quant_mode == SP_QUANT_MX_BLOCK) return static_cast<size_t>(H) / kMxBlock;
   return 0;
-}
-
-bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
-
-bool overlap(const void* a, size_t an, const void* b, size_t bn) {
-  if (!a || !b || an == 0 || bn == 0) return false;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + bn && b0 < a0 + an;
 }
 
 struct Plan {
@@ -916,126 +792,6 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   return SP_OK;
 }
 
-int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
-                        const void* const* shard_scales, void* out, void* out_scale,
-                        void* stream) {
-  if (!g) return fail(SP_ERR_NULL, "gather descriptor is NULL");
-  if (g->tp < 1 || g->tp > kMaxTp) return fail(SP_ERR_SHAPE, "tp=%d outside [1, %d]", g->tp, kMaxTp);
-  const int64_t S = g->shard_rows, H = g->hidden, T = g->num_tokens;
-  if (S < 0 || S > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld outside [0, 2^31)", (long long)S);
-  if (H < 8 || H > kMaxHidden || H % 8 != 0)
-    return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, %d]", (long long)H, kMaxHidden);
-  if (T < 0 || T > g->tp * S || T > INT32_MAX)
-    return fail(SP_ERR_SHAPE, "num_tokens=%lld outside [0, tp*S=%lld]", (long long)T, (long long)(g->tp * S));
-  const size_t row_bytes = row_bytes_of(g->dtype, H);
-  if (row_bytes == 0) return fail(SP_ERR_DTYPE, "dtype=%d unknown", g->dtype);
-  if (g->dtype == SP_FP4_E2M1 && H % 16 != 0)
-    return fail(SP_ERR_SHAPE, "hidden=%lld must be a multiple of 16 for e2m1 rows", (long long)H);
-  const int64_t sb = g->scale_row_bytes;
-  if (sb < 0 || sb > 65536)
-    return fail(SP_ERR_SHAPE, "scale_row_bytes=%lld outside [0, 65536]", (long long)sb);
-  if (T == 0) return SP_OK;
-  if (!shards || !out) return fail(SP_ERR_NULL, "shards and out must be non-NULL");
-  if ((shard_scales == nullptr) != (out_scale == nullptr) || (shard_scales == nullptr) != (sb == 0))
-    return fail(SP_ERR_NULL, "shard_scales, out_scale and scale_row_bytes must be all given or all none");
-  // 16-byte accesses when rows are a multiple of 16 bytes, else 8-byte ones;
-  // every row start must be aligned to the access width
-  const int B = row_bytes % 16 == 0 ? 16 : 8;
-  const uintptr_t amask = static_cast<uintptr_t>(B - 1);
-  if (reinterpret_cast<uintptr_t>(out) & amask)
-    return fail(SP_ERR_ALIGN, "out %p is not %d-byte aligned", out, B);
-  if (out_scale && sb == 4 && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
-    return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", out_scale);
-  const size_t out_n = static_cast<size_t>(T) * row_bytes;
-  GArgs ga;
-  memset(&ga, 0, sizeof ga);
-  for (int q = 0; q < g->tp; ++q) {
-    if (!shards[q]) return fail(SP_ERR_NULL, "shards[%d] is NULL", q);
-    if (reinterpret_cast<uintptr_t>(shards[q]) & amask)
-      return fail(SP_ERR_ALIGN, "shards[%d] %p is not %d-byte aligned", q, shards[q], B);
-    if (overlap(out, out_n, shards[q], static_cast<size_t>(S) * row_bytes))
-      return fail(SP_ERR_SHAPE, "out overlaps shards[%d]", q);
-    ga.src[q] = static_cast<const char*>(shards[q]);
-    if (shard_scales) {
-      if (!shard_scales[q]) return fail(SP_ERR_NULL, "shard_scales[%d] is NULL", q);
-      if (sb == 4 && (reinterpret_cast<uintptr_t>(shard_scales[q]) & 3u))
-        return fail(SP_ERR_ALIGN, "shard_scales[%d] is not 4-byte aligned", q);
-      if (overlap(out_scale, static_cast<size_t>(T * sb), shard_scales[q], static_cast<size_t>(S * sb)))
-        return fail(SP_ERR_SHAPE, "out_scale overlaps shard_scales[%d]", q);
-      ga.ssrc[q] = static_cast<const char*>(shard_scales[q]);
-    }
-  }
-  ga.out = static_cast<char*>(out);
-  ga.out_scale = static_cast<char*>(out_scale);
-  ga.S = S;
-  ga.row_bytes = static_cast<uint32_t>(row_bytes);
-  ga.scale_row_bytes = static_cast<uint32_t>(sb);
-  int nt = static_cast<int>((row_bytes / B + 63) / 64 * 64);
-  nt = nt > kMaxThreads ? kMaxThreads : nt;
-  void* args[] = {&ga};
-  const void* fn = B == 16 ? reinterpret_cast<const void*>(&gather_kernel<16>)
-                           : reinterpret_cast<const void*>(&gather_kernel<8>);
-  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(T)), dim3(static_cast<unsigned>(nt)), args,
-                                   0, static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return fail(SP_ERR_HIP, "gather launch failed: %s", hipGetErrorString(err));
-  return SP_OK;
-}
-
-int sp_fc2_regroup(const sp_fc2_problem* f, const void* const* src, void* const* dst, void* stream) {
-  if (!f) return fail(SP_ERR_NULL, "fc2 descriptor is NULL");
-  const int G = f->global_tp, P = f->otp;
-  if (G < 2 || G > kMaxTp) return fail(SP_ERR_SHAPE, "global_tp=%d outside [2, %d]", G, kMaxTp);
-  if (P < 1 || P >= G || G % P != 0)
-    return fail(SP_ERR_SHAPE, "otp=%d must divide global_tp=%d and be smaller", P, G);
-  if (f->reserved != 0) return fail(SP_ERR_UNSUPPORTED, "reserved field must be 0");
-  const size_t e = elt_size(f->dtype);
-  if (e == 0) return fail(SP_ERR_DTYPE, "dtype=%d unsupported", f->dtype);
-  const int64_t N = f->tokens, C = f->cols;
-  if (N < 0 || N % G != 0 || N > INT32_MAX) return fail(SP_ERR_SHAPE, "tokens=%lld must be a multiple of %d", (long long)N, G);
-  if (C < 1 || (C * static_cast<int64_t>(e)) % 4 != 0 || C * static_cast<int64_t>(e) * (G / P) > (1ll << 30))
-    return fail(SP_ERR_SHAPE, "cols=%lld gives rows that are not a multiple of 4 bytes", (long long)C);
-  if (static_cast<int64_t>(P) * N > static_cast<int64_t>(UINT32_MAX))
-    return fail(SP_ERR_SHAPE, "otp * tokens exceeds the grid limit");
-  if (N == 0) return SP_OK;
-  if (!src || !dst) return fail(SP_ERR_NULL, "src and dst must be non-NULL");
-  const int odp = G / P;
-  const size_t piece = static_cast<size_t>(C) * e;
-  const int B = piece % 16 == 0 ? 16 : 4;
-  const uintptr_t amask = static_cast<uintptr_t>(B - 1);
-  const size_t src_n = static_cast<size_t>(N) * piece, dst_n = static_cast<size_t>(N / odp) * piece * odp;
-  FArgs fa;
-  memset(&fa, 0, sizeof fa);
-  for (int q = 0; q < G; ++q) {
-    if (!src[q] || !dst[q]) return fail(SP_ERR_NULL, "src[%d] or dst[%d] is NULL", q, q);
-    if ((reinterpret_cast<uintptr_t>(src[q]) | reinterpret_cast<uintptr_t>(dst[q])) & amask)
-      return fail(SP_ERR_ALIGN, "src[%d] / dst[%d] not %d-byte aligned", q, q, B);
-    fa.src[q] = static_cast<const char*>(src[q]);
-    fa.dst[q] = static_cast<char*>(dst[q]);
-  }
-  for (int r = 0; r < G; ++r)
-    for (int q = 0; q < G; ++q) {
-      if (overlap(dst[r], dst_n, src[q], src_n)) return fail(SP_ERR_SHAPE, "dst[%d] overlaps src[%d]", r, q);
-      if (q != r && overlap(dst[r], dst_n, dst[q], dst_n))
-        return fail(SP_ERR_SHAPE, "dst[%d] overlaps dst[%d]", r, q);
-    }
-  fa.odp = odp;
-  fa.seg_rows = static_cast<int32_t>(N / G);
-  fa.dst_rows = static_cast<int32_t>(N / odp);
-  fa.piece = static_cast<uint32_t>(piece);
-  int nt = static_cast<int>((piece * odp / B + 63) / 64 * 64);
-  nt = nt > kMaxThreads ? kMaxThreads : nt;
-  if (static_cast<int64_t>(P) * N * nt > static_cast<int64_t>(UINT32_MAX))
-    return fail(SP_ERR_SHAPE, "otp * tokens * %d threads exceeds the dispatch limit", nt);
-  void* args[] = {&fa};
-  const void* fn = B == 16 ? reinterpret_cast<const void*>(&fc2_regroup_kernel<16>)
-                           : reinterpret_cast<const void*>(&fc2_regroup_kernel<4>);
-  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(G) * (N / odp));
-  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(static_cast<unsigned>(nt)), args, 0,
-                                   static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return fail(SP_ERR_HIP, "fc2 regroup launch failed: %s", hipGetErrorString(err));
-  return SP_OK;
-}
-
 int sp_shard_geometry(int64_t num_tokens, int64_t num_tokens_pad, int32_t tp, int32_t rank,
                       int64_t* shard_rows, int64_t* local_start, int64_t* valid_rows) {
   if (!shard_rows || !local_start || !valid_rows) return fail(SP_ERR_NULL, "output pointer is NULL");
@@ -1066,6 +822,6 @@ const char* sp_error_string(int status) {
   return "unknown status";
 }
 
-const char* sp_last_error(void) { return g_last_error; }
+const char* sp_last_error(void) { return sprms::g_last_error; }
 
 }  // extern "C"

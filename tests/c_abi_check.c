@@ -48,6 +48,18 @@ int main(void) {
         SP_ERR_UNSUPPORTED);
   CHECK(sp_validate(&p, partials, residual, weight, NULL, 1e-6f, SP_QUANT_NONE, NULL, out, NULL) ==
         SP_ERR_DTYPE);
+  /* the layout calls through their C descriptors: empty problems are no-ops,
+   * invalid ones are refused before anything is enqueued */
+  sp_gather_problem g = {4, SP_BF16, 0, 4096, 0, 0};
+  CHECK(sp_all_gather_unpad(&g, NULL, NULL, NULL, NULL, NULL) == SP_OK);
+  sp_fc2_problem f = {4, 2, SP_BF16, -1, 0, 1024};
+  CHECK(sp_fc2_regroup(&f, NULL, NULL, NULL) == SP_OK);
+  f.otp = 3;
+  CHECK(sp_fc2_regroup(&f, NULL, NULL, NULL) == SP_ERR_SHAPE);
+  sp_dsacp_problem d = {16, SP_BF16, -1, 0, 0, 1024};
+  CHECK(sp_dsacp_heads_to_tokens(&d, NULL, NULL, NULL) == SP_OK);
+  d.rank = 16;
+  CHECK(sp_dsacp_heads_to_tokens(&d, NULL, NULL, NULL) == SP_ERR_SHAPE);
   CHECK(strcmp(sp_error_string(SP_OK), "success") == 0);
   printf("c abi ok\n");
   return 0;

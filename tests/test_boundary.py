@@ -184,10 +184,10 @@ def test_gather_empty_is_a_no_op():
     assert _gather(S=0, T=0)[0] == sp.SP_OK
 
 
-def _fc2(G=4, otp=2, dtype=sp.SP_BF16, N=8, Cc=8, reserved=0, src=None, dst=None):
+def _fc2(G=4, otp=2, dtype=sp.SP_BF16, N=8, Cc=8, rank=-1, src=None, dst=None):
     import ctypes as C
     lib = sp.load()
-    f = sp.sp_fc2_problem(global_tp=G, otp=otp, dtype=dtype, reserved=reserved, tokens=N, cols=Cc)
+    f = sp.sp_fc2_problem(global_tp=G, otp=otp, dtype=dtype, rank=rank, tokens=N, cols=Cc)
     src = src if src is not None else [BASE + q * GB for q in range(G)]
     dst = dst if dst is not None else [BASE + (G + q) * GB for q in range(G)]
     s = (C.c_void_p * len(src))(*src)
@@ -201,7 +201,13 @@ def _fc2(G=4, otp=2, dtype=sp.SP_BF16, N=8, Cc=8, reserved=0, src=None, dst=None
     (dict(otp=4), sp.SP_ERR_SHAPE),                       # otp == G
     (dict(otp=3), sp.SP_ERR_SHAPE),                       # does not divide G
     (dict(otp=0), sp.SP_ERR_SHAPE),
-    (dict(reserved=1), sp.SP_ERR_UNSUPPORTED),
+    (dict(rank=4), sp.SP_ERR_SHAPE),
+    (dict(rank=-2), sp.SP_ERR_SHAPE),
+    (dict(rank=1, dst=[BASE + 4 * GB, 0, BASE + 6 * GB, BASE + 7 * GB]), sp.SP_ERR_NULL),
+    # only dst[rank] is checked: NULL and overlapping unwritten entries are ignored, so the
+    # call gets as far as the misaligned source
+    (dict(rank=1, dst=[0, BASE + 5 * GB, BASE + 5 * GB, 0],
+          src=[BASE, BASE + GB + 4, BASE + 2 * GB, BASE + 3 * GB]), sp.SP_ERR_ALIGN),
     (dict(dtype=sp.SP_FP4_E2M1), sp.SP_ERR_DTYPE),
     (dict(dtype=7), sp.SP_ERR_DTYPE),
     (dict(N=10), sp.SP_ERR_SHAPE),                        # not a multiple of G
@@ -224,6 +230,62 @@ def test_fc2_regroup_rejects_invalid_problems(case, expect):
     assert status == expect, msg
     if case.get("N") == 1 << 27:
         assert "dispatch" in msg
+    if case.get("rank") == 1 and case.get("src"):
+        assert "src[1]" in msg
+
+
+def test_fc2_rank_mode_checks_only_its_own_destination():
+    # dst[1] sits on top of dst[0], which rank 0's call does not write: the
+    # call passes the pointer checks and stops at the dispatch limit
+    status, msg = _fc2(G=2, otp=1, rank=0, N=1 << 27, Cc=64, src=[BASE, BASE + 64 * GB],
+                       dst=[BASE + 128 * GB, BASE + 128 * GB + 16])
+    assert status == sp.SP_ERR_SHAPE and "dispatch" in msg, msg
+
+
+def _dsacp(tp=4, dtype=sp.SP_BF16, rank=-1, reserved=0, S=8, D=8, attn=None, out=None):
+    import ctypes as C
+    lib = sp.load()
+    f = sp.sp_dsacp_problem(tp=tp, dtype=dtype, rank=rank, reserved=reserved, shard_rows=S,
+                            head_cols=D)
+    attn = attn if attn is not None else [BASE + q * GB for q in range(max(tp, 1))]
+    out = out if out is not None else [BASE + (64 + q) * GB for q in range(max(tp, 1))]
+    a = (C.c_void_p * len(attn))(*attn)
+    o = (C.c_void_p * len(out))(*out)
+    return lib.sp_dsacp_heads_to_tokens(C.byref(f), a, o, None), sp.sp_last_error()
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(tp=0), sp.SP_ERR_SHAPE),
+    (dict(tp=65, attn=[BASE] * 65, out=[BASE + GB] * 65), sp.SP_ERR_SHAPE),
+    (dict(rank=4), sp.SP_ERR_SHAPE),
+    (dict(rank=-2), sp.SP_ERR_SHAPE),
+    (dict(reserved=3), sp.SP_ERR_UNSUPPORTED),
+    (dict(dtype=sp.SP_FP4_E2M1), sp.SP_ERR_DTYPE),
+    (dict(dtype=9), sp.SP_ERR_DTYPE),
+    (dict(S=-1), sp.SP_ERR_SHAPE),
+    (dict(S=1 << 29), sp.SP_ERR_SHAPE),                  # tp*S = 2^31
+    (dict(D=0), sp.SP_ERR_SHAPE),
+    (dict(D=1), sp.SP_ERR_SHAPE),                        # 2-byte pieces
+    (dict(attn=[BASE, 0, BASE + 2 * GB, BASE + 3 * GB]), sp.SP_ERR_NULL),
+    (dict(out=[BASE + 64 * GB, BASE + 65 * GB, 0, BASE + 67 * GB]), sp.SP_ERR_NULL),
+    (dict(attn=[BASE, BASE + GB, BASE + 2 * GB + 8, BASE + 3 * GB]), sp.SP_ERR_ALIGN),
+    (dict(D=2, out=[BASE + 64 * GB, BASE + 65 * GB + 2, BASE + 66 * GB, BASE + 67 * GB]),
+     sp.SP_ERR_ALIGN),                                   # 4-byte pieces, 2-byte offset
+    (dict(out=[BASE + 64 * GB, BASE + GB + 64, BASE + 66 * GB, BASE + 67 * GB]), sp.SP_ERR_SHAPE),
+    (dict(out=[BASE + 64 * GB, BASE + 65 * GB, BASE + 64 * GB + 32, BASE + 67 * GB]),
+     sp.SP_ERR_SHAPE),
+    (dict(rank=2, out=[0, 0, BASE + 66 * GB, 0], S=1 << 24, D=8), sp.SP_ERR_SHAPE),  # dispatch
+])
+def test_dsacp_rejects_invalid_problems(case, expect):
+    status, msg = _dsacp(**case)
+    assert status == expect, msg
+    if case.get("rank") == 2:
+        assert "dispatch" in msg
+
+
+def test_dsacp_empty_is_a_no_op():
+    assert _dsacp(S=0)[0] == sp.SP_OK
+    assert _dsacp(S=0, tp=1, attn=[BASE + 2], out=[BASE + GB + 2])[0] == sp.SP_OK
 
 
 def test_fc2_regroup_empty_is_a_no_op():
@@ -243,6 +305,13 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         sp.sp_reduce_add_rmsnorm(x, x[0], x[0, 0], None, 1e-6, 0, None, x[0], None, tp_rank=0,
                                  num_tokens=8)
+    with pytest.raises(ValueError):
+        sp.sp_all_gather_unpad([x[0], x[1]], None, torch.zeros((8, 8), dtype=torch.bfloat16),
+                               None, num_tokens=8)
+    with pytest.raises(ValueError):
+        sp.sp_fc2_regroup([x[0], x[1]], [x[0].clone(), x[1].clone()], otp=1)
+    with pytest.raises(ValueError):
+        sp.sp_dsacp_heads_to_tokens([x[0], x[1]], [x[0].clone(), x[1].clone()])
 
 
 def test_plain_c_client_compiles_links_and_runs(tmp_path):
