@@ -1,6 +1,7 @@
 """Benchmark of the fused shard path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5]
+                    [--path fused|gather|fc2|dsacp] [--quant mxfp8|mxfp4]
 
 One step = one call of sp_reduce_add_rmsnorm over the whole shard of the
 workload's timed rank (every stage of the path in one kernel), inputs
@@ -34,24 +35,27 @@ from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK, 
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + shard tokens/s for fused reduce-add-RMSNorm"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
-# sources of the fused kernel (the layout kernels live in csrc/layout.hip)
-KERNEL_SRCS = [os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc", f) for f in ("sprms.hip", "common.h")]
+# sources each measured kernel is built from: the fused kernel, and the
+# layout kernels (gather, regroupings)
+_CSRC = os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc")
+KERNEL_SRCS = {"fused": [os.path.join(_CSRC, f) for f in ("sprms.hip", "common.h")],
+               "layout": [os.path.join(_CSRC, f) for f in ("layout.hip", "common.h")]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
 QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3",
                4: "block-scaled (32-element E8M0 scales)"}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kind: str = "fused") -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[kind]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kind: str = "fused"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current source of the kernel; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
@@ -59,7 +63,7 @@ def measured_traffic(workload: str):
     if not m:
         return None
     rec = json.loads(m.group(1)).get(workload)
-    if not rec or rec.get("kernel_sha256_16") != kernel_hash():
+    if not rec or rec.get("kernel_sha256_16") != kernel_hash(kind):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -109,6 +113,53 @@ def setup_gather(w, dev):
     e = out.element_size()
     nbytes = 2 * T * (H * e + (4 if scaled else 0))  # read and write each gathered byte once
     return (shards, scales, out, out_scale), launch, nbytes, T
+
+
+FC2_OTP = 2  # the o_proj group size of the FlashComm2 worked example
+
+
+def setup_fc2(w, dev):
+    """FlashComm2 o_proj input regrouping, one rank's share: the workload's
+    tp ranks as the FlashComm2 group (G = tp, otp = 2), each holding its
+    H/G feature columns of all num_tokens_pad tokens in bf16; rank w.rank
+    pulls its [N/odp, odp*H/G] block from the G source buffers."""
+    G, N, H = w.tp, w.num_tokens_pad, w.hidden
+    Cc = H // G
+    odp = G // FC2_OTP
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_index + 1)
+    srcs = [torch.randn((N, Cc), generator=g, device=dev).to(torch.bfloat16) for _ in range(G)]
+    dsts = [None] * G
+    dsts[w.rank] = torch.empty((N // odp, odp * Cc), dtype=torch.bfloat16, device=dev)
+
+    def launch():
+        sp.sp_fc2_regroup(srcs, dsts, otp=FC2_OTP, rank=w.rank)
+
+    nbytes = 2 * (N // odp) * odp * Cc * 2  # read and write the block once
+    desc = (f"FlashComm2 regroup, rank {w.rank} of G={G}, otp={FC2_OTP}: [{N}, {Cc}] x {G} -> "
+            f"[{N // odp}, {odp * Cc}] bf16")
+    return (srcs, dsts), launch, nbytes, N // odp, desc
+
+
+def setup_dsacp(w, dev):
+    """DSA-CP o_proj input exchange, one rank's share: the workload's tp
+    ranks each hold their S shard tokens with every rank's heads, [S, H] in
+    bf16 (H = tp * D); rank w.rank pulls every token's head block, [tp*S, D]."""
+    tp, S, H = w.tp, w.shard_rows, w.hidden
+    D = H // tp
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_index + 2)
+    attn = [torch.randn((S, tp * D), generator=g, device=dev).to(torch.bfloat16) for _ in range(tp)]
+    outs = [None] * tp
+    outs[w.rank] = torch.empty((tp * S, D), dtype=torch.bfloat16, device=dev)
+
+    def launch():
+        sp.sp_dsacp_heads_to_tokens(attn, outs, rank=w.rank)
+
+    nbytes = 2 * tp * S * D * 2
+    desc = (f"DSA-CP head-to-token exchange, rank {w.rank} of tp={tp}: [{S}, {tp * D}] x {tp} -> "
+            f"[{tp * S}, {D}] bf16")
+    return (attn, outs), launch, nbytes, tp * S, desc
 
 
 def cpu_baseline(w, x, budget_s: float):
@@ -184,9 +235,11 @@ def main():
     ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
-    ap.add_argument("--path", default="fused", choices=["fused", "gather"],
+    ap.add_argument("--path", default="fused", choices=["fused", "gather", "fc2", "dsacp"],
                     help="fused: the shard kernel (the headline); gather: AllGather + unpad of "
-                         "every rank's shard output of the workload into [T, H] on this GPU")
+                         "every rank's shard output of the workload into [T, H] on this GPU; "
+                         "fc2 / dsacp: one rank's share of the FlashComm2 o_proj regroup or of "
+                         "the DSA-CP head-to-token exchange at the workload's tp, tokens and H")
     ap.add_argument("--quant", default=None, choices=["mxfp8", "mxfp4"],
                     help="replace the workload's output quantisation by block scaling "
                          "(32-element E8M0 scales) with e4m3 or e2m1 elements")
@@ -209,8 +262,17 @@ def main():
         w = dataclasses.replace(w, quant_mode=QUANT_MX_BLOCK, out_dtype=torch.uint8,
                                 fp4=args.quant == "mxfp4")
     sp.load()
+    desc = None
     if args.path == "gather":
         x, launch, nbytes, tokens = setup_gather(w, dev)
+        desc = (f"{w.name} AllGather + unpad of all {w.tp} shard outputs into "
+                f"[{w.num_tokens}, {w.hidden}] (+ per-row scales)")
+    elif args.path == "fc2":
+        x, launch, nbytes, tokens, desc = setup_fc2(w, dev)
+        desc = f"{w.name} {desc}"
+    elif args.path == "dsacp":
+        x, launch, nbytes, tokens, desc = setup_dsacp(w, dev)
+        desc = f"{w.name} {desc}"
     else:
         x, launch, _ = setup(w, dev)
         nbytes, tokens = w.algorithmic_bytes(), w.valid_rows()
@@ -251,10 +313,12 @@ def main():
     value = nbytes / (ms_per_step / 1000.0) / 1e9
     achieved = nbytes / (avg_ms / 1000.0) / 1e9
     traffic = measured_traffic(w.name if args.path == "fused" and not args.quant else
-                               f"{w.name}-{args.path}-{args.quant}")
+                               f"{w.name}-{args.path}-{args.quant}",
+                               "fused" if args.path == "fused" else "layout")
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.path == "fused" else
+        f"achieved HBM GB/s (% of MI355X peak) for {args.path} (one rank's share)",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -264,13 +328,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the fused path computes in fp32; the layout paths move elements unchanged
+        "dtype": ("f32" if args.path == "fused" else "bf16" if args.path in ("fc2", "dsacp")
+                  else {torch.uint8: "u8", torch.bfloat16: "bf16"}.get(w.out_dtype, "f32")),
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.name}: {w.description}" if args.path == "fused" else
-                         f"{w.name} AllGather + unpad of all {w.tp} shard outputs into "
-                         f"[{w.num_tokens}, {w.hidden}] (+ per-row scales)"),
-            "path": "sp_reduce_add_rmsnorm" if args.path == "fused" else "sp_all_gather_unpad",
+            "workload": f"{w.name}: {w.description}" if args.path == "fused" else desc,
+            "path": {"fused": "sp_reduce_add_rmsnorm", "gather": "sp_all_gather_unpad",
+                     "fc2": "sp_fc2_regroup", "dsacp": "sp_dsacp_heads_to_tokens"}[args.path],
             "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
             "shard_rows": w.shard_rows, "hidden": w.hidden,
             "quant": QUANT_NAMES[w.quant_mode] + (

@@ -184,3 +184,32 @@ def test_sequence_parallel_tail_equals_all_reduce_path(dev):
     assert within_rounding(got_o, y - err_y, y + err_y, bf16_round).all()
     assert (to_host(out) == ref["out"]).mean() >= 0.99
     assert np.isfinite(got_o).all()
+
+
+@pytest.mark.parametrize("tp,S,H,T", [
+    (4, 40, 160, 4 * 40 - 7),      # 5 E8M0 bytes per row: byte-wise scale copy
+    (4, 40, 5120, 4 * 40 - 7),     # 160 bytes per row: word-wise scale copy
+    (3, 9, 96, 25),                # 3 bytes per row
+])
+def test_gather_block_scales_match_oracle(dev, tp, S, H, T):
+    say(f"gather with E8M0 block scales tp={tp} S={S} H={H} T={T}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(H + T)
+    shards = [torch.randint(0, 256, (S, H), generator=g, device=dev, dtype=torch.uint8)
+              for _ in range(tp)]
+    sc = [torch.randint(0, 256, (S, H // 32), generator=g, device=dev, dtype=torch.uint8)
+          for _ in range(tp)]
+    out = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    osc_buf = torch.full((T * (H // 32) + 2,), 0xA5, dtype=torch.uint8, device=dev)
+    osc = osc_buf[1:T * (H // 32) + 1].view(T, H // 32)   # 1-byte offset: byte-wise copy
+    osc_al = torch.full((T, H // 32), 0xA5, dtype=torch.uint8, device=dev)
+    sp.sp_all_gather_unpad(shards, sc, out, osc, num_tokens=T)
+    sp.sp_all_gather_unpad(shards, sc, out, osc_al, num_tokens=T)
+    torch.cuda.synchronize()
+    ref, ref_sc = oracle.all_gather_unpad([t.cpu().numpy() for t in shards],
+                                          [t.cpu().numpy() for t in sc], num_tokens=T)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+    np.testing.assert_array_equal(osc.cpu().numpy(), ref_sc)
+    np.testing.assert_array_equal(osc_al.cpu().numpy(), ref_sc)
+    b = osc_buf.cpu().numpy()
+    assert b[0] == 0xA5 and b[-1] == 0xA5
