@@ -197,6 +197,12 @@ def cpu_baseline(w, x, budget_s: float):
     n = int(min(S, max(8, budget_s / max(t_probe, 1e-9))))
     secs = run(n)
     per_row = w.algorithmic_bytes() / S  # all rows valid in the timed workloads
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(n * per_row / secs / 1e9, 4),
         "unit": "GB/s",
@@ -206,6 +212,7 @@ def cpu_baseline(w, x, budget_s: float):
                   f"{n / secs:.1f} shard tokens/s",
         "tokens_per_s": round(n / secs, 2),
         "seconds": round(secs, 2),
+        "host": {"cpu": model, "logical_cpus": os.cpu_count()},
     }
 
 

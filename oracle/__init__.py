@@ -29,6 +29,7 @@ from .oracle import (  # noqa: F401
     e4m3_to_double,
     fc2_batch_ids,
     fc2_regroup,
+    matmul_scatter,
     reduce_add_rmsnorm,
     shard_geometry,
 )

@@ -89,6 +89,9 @@ def _load():
     lib.orc_fc2_regroup.restype = C.c_int
     lib.orc_dsacp_heads_to_tokens.argtypes = [i32, i64, i64, C.POINTER(vp), C.POINTER(vp)]
     lib.orc_dsacp_heads_to_tokens.restype = C.c_int
+    lib.orc_matmul_scatter.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i64, vp,
+                                       C.POINTER(vp)]
+    lib.orc_matmul_scatter.restype = C.c_int
     lib.orc_e2m1_from_double.argtypes = [C.c_double]
     lib.orc_e2m1_from_double.restype = C.c_uint8
     lib.orc_e2m1_to_double.argtypes = [C.c_uint8]
@@ -299,3 +302,28 @@ def dsacp_heads_to_tokens(attn):
     if rc != 0:
         raise OracleError(f"orc_dsacp_heads_to_tokens failed: {rc}")
     return outs
+
+
+def matmul_scatter(x, w, *, tp, rank, out_dtype=ORC_F32, rows=None, dst=None):
+    """Rank `rank`'s row-parallel GEMM P = x w^T (x [tp*S, K], w [N, K], bf16
+    bits as uint16) written into the tp receive buffers [tp][S][N] (slot
+    `rank` of each).  ``dst`` may be given to collect several ranks' slots;
+    ``rows`` selects the token rows computed."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    if M % tp or w.shape[1] != K:
+        raise OracleError("x must be [tp*S, K] and w [N, K]")
+    S = M // tp
+    dt = np.float32 if out_dtype == ORC_F32 else np.uint16
+    if dst is None:
+        dst = [np.zeros((tp, S, N), dtype=dt) for _ in range(tp)]
+    dp = (C.c_void_p * tp)(*[d.ctypes.data for d in dst])
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    rc = lib.orc_matmul_scatter(tp, rank, S, K, N, out_dtype, _ptr(x), _ptr(w),
+                                0 if r is None else len(r), None if r is None else _ptr(r), dp)
+    if rc != 0:
+        raise OracleError(f"orc_matmul_scatter failed: {rc}")
+    return dst

@@ -501,3 +501,44 @@ int orc_dsacp_heads_to_tokens(int32_t tp, int64_t S, int64_t piece, const void* 
   free(send);
   return ORC_OK;
 }
+
+/* ------------------------------- row-parallel GEMM + scatter (the producer) */
+
+/* [SPquant] §二, the GEMM + ReduceScatter at a block's exit, with o_proj
+ * split along K over the tp ranks ([LongCat], o_proj TP K-axis split).
+ * Rank q holds x_q [M][K] (its K-slice of the input for all M = tp*S
+ * tokens) and w_q [N][K] (its K-slice of the weight, one row per output
+ * column) and computes its unreduced partial P_q = x_q * w_q^T, [M][N].
+ * The ReduceScatter along the tokens hands row block r (rows r*S .. r*S+S-1)
+ * to rank r, which sums the tp blocks it receives; before that sum rank r
+ * holds them as [tp][S][N], slot q coming from rank q.  This writes rank q's
+ * share of those buffers: dst[r] slot q row s = P_q[r*S + s], each element
+ * the dot product of bf16 inputs summed in fp64 (every product is exact)
+ * and rounded once to out_dtype.  rows (n_rows entries, NULL = all M)
+ * selects the token rows m computed; other rows of dst are not touched. */
+int orc_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N, int32_t out_dtype,
+                       const uint16_t* x, const uint16_t* w, int64_t n_rows, const int64_t* rows,
+                       void* const* dst) {
+  if (tp < 1 || rank < 0 || rank >= tp || S < 0 || K < 1 || N < 1) return ORC_ERR_SHAPE;
+  if (out_dtype != ORC_BF16 && out_dtype != ORC_F32) return ORC_ERR_DTYPE;
+  const int64_t M = (int64_t)tp * S;
+  const int64_t count = rows ? n_rows : M;
+  if (count == 0) return ORC_OK;
+  if (!x || !w || !dst) return ORC_ERR_NULL;
+  for (int r = 0; r < tp; ++r)
+    if (!dst[r]) return ORC_ERR_NULL;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows && (rows[i] < 0 || rows[i] >= M)) return ORC_ERR_SHAPE;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t m = rows ? rows[i] : i;
+    const int64_t r = m / S;     /* destination rank of this token */
+    const int64_t s = m - r * S; /* its row in that rank's shard */
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += orc_bf16_to_double(x[m * K + k]) * orc_bf16_to_double(w[n * K + k]);
+      store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc);
+    }
+  }
+  return ORC_OK;
+}

@@ -107,6 +107,14 @@ int orc_fc2_regroup(int32_t G, int32_t otp, int64_t N, int64_t C, int32_t elt,
 int orc_dsacp_heads_to_tokens(int32_t tp, int64_t S, int64_t piece, const void* const* attn,
                               void* const* out);
 
+/* Row-parallel GEMM of rank `rank` with its ReduceScatter destinations
+ * ([SPquant] §二): P = x w^T with x [tp*S][K], w [N][K] (bf16 bits); dst[r]
+ * is rank r's [tp][S][N] receive buffer (out_dtype ORC_BF16 or ORC_F32),
+ * slot `rank` row s = P[r*S + s].  rows selects token rows (NULL = all). */
+int orc_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N, int32_t out_dtype,
+                       const uint16_t* x, const uint16_t* w, int64_t n_rows, const int64_t* rows,
+                       void* const* dst);
+
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
 double orc_bf16_to_double(uint16_t bits);

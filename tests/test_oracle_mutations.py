@@ -50,6 +50,12 @@ MUTATIONS = {
                               "memcpy((char*)out[q] + (size_t)p * chunk, send + (size_t)p * chunk, chunk);"),
     "dsacp_head_major_view": ("((size_t)s * (size_t)tp + (size_t)q) * (size_t)piece",
                               "((size_t)q * (size_t)S + (size_t)s) * (size_t)piece"),
+    "mm_slot_of_destination": ("store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc);",
+                               "store(dst[r], out_dtype, ((int64_t)r * S + s) * N + n, acc);"),
+    "mm_round_robin_tokens": ("const int64_t r = m / S;     /* destination rank of this token */\n"
+                              "    const int64_t s = m - r * S; /* its row in that rank's shard */",
+                              "const int64_t r = m % tp;\n    const int64_t s = m / tp;"),
+    "mm_weight_transposed": ("orc_bf16_to_double(w[n * K + k])", "orc_bf16_to_double(w[k * N + n])"),
     "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
                              "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
     "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",

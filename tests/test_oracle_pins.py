@@ -695,3 +695,100 @@ def test_dsacp_exchange_is_undone_by_the_plain_all_to_all(tp, S, D):
     back = oracle.fc2_regroup(oracle.dsacp_heads_to_tokens(attn), otp=1)
     for p in range(tp):
         np.testing.assert_array_equal(back[p], attn[p])
+
+
+# ------------------------------- row-parallel GEMM + scatter (the producer)
+
+
+def _bf16_bits(a):
+    a = np.asarray(a, dtype=np.float32)
+    assert np.array_equal(a, (a.view(np.uint32) & 0xFFFF0000).view(np.float32)), "not bf16-exact"
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_matmul_scatter_brute_force():
+    # every element against a plain triple loop over exact integers and halves
+    rng = np.random.default_rng(5)
+    tp, S, K, N = 3, 2, 5, 4
+    x = rng.integers(-6, 7, (tp * S, K)) / 2.0
+    w = rng.integers(-5, 6, (N, K)) / 2.0
+    for rank in range(tp):
+        dst = oracle.matmul_scatter(_bf16_bits(x), _bf16_bits(w), tp=tp, rank=rank)
+        for m in range(tp * S):
+            r, s = divmod(m, S)
+            for n in range(N):
+                want = 0.0
+                for k in range(K):
+                    want += x[m][k] * w[n][k]
+                assert dst[r][rank][s][n] == want, (rank, m, n)
+                for q in range(tp):
+                    if q != rank:
+                        assert dst[r][q][s][n] == 0.0
+
+
+@pytest.mark.parametrize("tp,S,Kr,N", [(2, 3, 4, 5), (4, 2, 3, 6), (8, 1, 2, 3)])
+def test_matmul_reduce_scatter_equals_all_reduce(tp, S, Kr, N):
+    # [SPquant] §二 / [SP/FC] §2.2: each rank's K-slice GEMM, scattered by token
+    # block and summed on the destination, equals the full GEMM's row block
+    rng = np.random.default_rng(tp * 10 + S)
+    X = rng.integers(-4, 5, (tp * S, tp * Kr)).astype(np.float32)   # full input
+    W = rng.integers(-4, 5, (N, tp * Kr)).astype(np.float32)        # full weight [N, K]
+    dst = None
+    for q in range(tp):
+        dst = oracle.matmul_scatter(_bf16_bits(X[:, q * Kr:(q + 1) * Kr]),
+                                    _bf16_bits(W[:, q * Kr:(q + 1) * Kr]), tp=tp, rank=q, dst=dst)
+    full = X.astype(np.float64) @ W.T.astype(np.float64)
+    for r in range(tp):
+        np.testing.assert_array_equal(dst[r].astype(np.float64).sum(0), full[r * S:(r + 1) * S])
+
+
+def test_matmul_scatter_places_token_blocks_by_destination():
+    # x row m carries its token index; w picks it out: element = m.  Rank q's
+    # block for destination r must sit in slot q of dst[r] (rows r*S + s)
+    tp, S, K, N = 4, 3, 2, 2
+    x = np.zeros((tp * S, K), np.float32)
+    x[:, 0] = np.arange(tp * S)
+    w = np.zeros((N, K), np.float32)
+    w[:, 0] = 1.0
+    for q in range(tp):
+        dst = oracle.matmul_scatter(_bf16_bits(x * (q + 1)), _bf16_bits(w), tp=tp, rank=q)
+        for r in range(tp):
+            for s in range(S):
+                np.testing.assert_array_equal(dst[r][q][s], (q + 1) * (r * S + s))
+
+
+def test_matmul_scatter_rows_and_bf16_rounding():
+    # bf16 output is the once-rounded exact dot product; rows selects tokens
+    x = np.array([[1.0, 2.0 ** -8], [3.0, 1.0]], np.float32)     # 1 + 2^-8 is a bf16 tie
+    w = np.array([[1.0, 1.0]], np.float32)
+    dst = oracle.matmul_scatter(_bf16_bits(x), _bf16_bits(w), tp=1, rank=0,
+                                out_dtype=oracle.ORC_BF16, rows=[0])
+    assert dst[0][0][0][0] == 0x3F80        # ties to even: 1.0
+    assert dst[0][0][1][0] == 0             # row 1 not computed
+    d32 = oracle.matmul_scatter(_bf16_bits(x), _bf16_bits(w), tp=1, rank=0)
+    assert d32[0][0][0][0] == np.float32(1 + 2.0 ** -8) and d32[0][0][1][0] == 4.0
+
+
+def test_producer_feeds_the_fused_path():
+    # the receive buffer of rank r, reduced by the fused oracle, equals the
+    # fused oracle on the AllReduced GEMM output (integers: exact)
+    tp, S, Kr, N = 4, 3, 8, 32
+    rng = np.random.default_rng(77)
+    X = rng.integers(-3, 4, (tp * S, tp * Kr)).astype(np.float32)
+    W = rng.integers(-3, 4, (N, tp * Kr)).astype(np.float32)
+    R = _bf16_bits(rng.integers(-4, 5, (tp * S, N)).astype(np.float32))
+    g = _bf16_bits(np.ones(N, np.float32))
+    dst = None
+    for q in range(tp):
+        dst = oracle.matmul_scatter(_bf16_bits(X[:, q * Kr:(q + 1) * Kr]),
+                                    _bf16_bits(W[:, q * Kr:(q + 1) * Kr]), tp=tp, rank=q, dst=dst)
+    full = (X.astype(np.float64) @ W.T.astype(np.float64)).astype(np.float32)[None]
+    T = tp * S - 2
+    for r in range(tp):
+        a = oracle.reduce_add_rmsnorm(dst[r], R, g, None, 1e-6, oracle.QUANT_NONE, None,
+                                      tp_rank=r, num_tokens=T)
+        v = max(0, min(S, T - r * S))
+        b = oracle.reduce_add_rmsnorm(full[:, r * S:(r + 1) * S].copy(), R[r * S:(r + 1) * S], g,
+                                      None, 1e-6, oracle.QUANT_NONE, None, tp_rank=0, num_tokens=v)
+        np.testing.assert_array_equal(a["out"], b["out"])
+        np.testing.assert_array_equal(a["residual_out"], b["residual_out"])
