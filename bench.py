@@ -162,6 +162,44 @@ def setup_dsacp(w, dev):
     return (attn, outs), launch, nbytes, tp * S, desc
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD published
+
+
+def setup_gemm(w, dev):
+    """One rank's producer GEMM at the workload's shape: x [T_pad, H/tp] and
+    the weight [H, H/tp] in bf16, bf16 partials written into slot `rank` of
+    the tp receive buffers [tp, S, H] (o_proj split along K; K = H/tp)."""
+    tp, S, H = w.tp, w.shard_rows, w.hidden
+    M, K = tp * S, H // tp
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_index + 3)
+    x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    wt = (torch.randn((H, K), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    dsts = [torch.empty((tp, S, H), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+
+    def launch():
+        sp.sp_matmul_scatter(x, wt, dsts, rank=w.rank)
+
+    desc = (f"producer GEMM of rank {w.rank} of tp={tp}: [{M}, {K}] x [{H}, {K}]^T bf16, fp32 "
+            f"accumulation, bf16 partials scattered to {tp} receive buffers")
+    return (x, wt, dsts), launch, 2 * M * K * H, M, desc
+
+
+def library_gemm_us(x, wt, steps=20):
+    """hipBLASLt (torch's linear) on the same operands, for context only."""
+    import torch.nn.functional as F
+    for _ in range(3):
+        F.linear(x, wt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        F.linear(x, wt)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000 / steps
+
+
 def cpu_baseline(w, x, budget_s: float):
     """The C oracle on the first rows of the same shard, single-threaded."""
     import oracle  # CPU checker; only this leg of the benchmark uses it
@@ -242,11 +280,13 @@ def main():
     ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
-    ap.add_argument("--path", default="fused", choices=["fused", "gather", "fc2", "dsacp"],
+    ap.add_argument("--path", default="fused", choices=["fused", "gather", "fc2", "dsacp", "gemm"],
                     help="fused: the shard kernel (the headline); gather: AllGather + unpad of "
                          "every rank's shard output of the workload into [T, H] on this GPU; "
                          "fc2 / dsacp: one rank's share of the FlashComm2 o_proj regroup or of "
-                         "the DSA-CP head-to-token exchange at the workload's tp, tokens and H")
+                         "the DSA-CP head-to-token exchange at the workload's tp, tokens and H; "
+                         "gemm: one rank's producer GEMM (o_proj split along K) with its "
+                         "ReduceScatter destinations")
     ap.add_argument("--quant", default=None, choices=["mxfp8", "mxfp4"],
                     help="replace the workload's output quantisation by block scaling "
                          "(32-element E8M0 scales) with e4m3 or e2m1 elements")
@@ -279,6 +319,9 @@ def main():
         desc = f"{w.name} {desc}"
     elif args.path == "dsacp":
         x, launch, nbytes, tokens, desc = setup_dsacp(w, dev)
+        desc = f"{w.name} {desc}"
+    elif args.path == "gemm":
+        x, launch, nbytes, tokens, desc = setup_gemm(w, dev)  # nbytes: flops here
         desc = f"{w.name} {desc}"
     else:
         x, launch, _ = setup(w, dev)
@@ -317,17 +360,21 @@ def main():
     per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
 
     ms_per_step = wall * 1000.0 / args.steps
-    value = nbytes / (ms_per_step / 1000.0) / 1e9
-    achieved = nbytes / (avg_ms / 1000.0) / 1e9
+    gemm = args.path == "gemm"
+    scale = 1e12 if gemm else 1e9   # TFLOP/s for the GEMM, GB/s for the rest
+    peak = MFMA_BF16_PEAK_TFLOPS if gemm else HBM_PEAK_GBS
+    value = nbytes / (ms_per_step / 1000.0) / scale
+    achieved = nbytes / (avg_ms / 1000.0) / scale
     traffic = measured_traffic(w.name if args.path == "fused" and not args.quant else
                                f"{w.name}-{args.path}-{args.quant}",
                                "fused" if args.path == "fused" else "layout")
 
     result = {
         "metric": METRIC if args.path == "fused" else
+        "achieved bf16 TFLOP/s (% of MI355X dense MFMA peak) for the producer GEMM" if gemm else
         f"achieved HBM GB/s (% of MI355X peak) for {args.path} (one rank's share)",
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": "TFLOP/s" if gemm else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -336,21 +383,22 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         # the fused path computes in fp32; the layout paths move elements unchanged
-        "dtype": ("f32" if args.path == "fused" else "bf16" if args.path in ("fc2", "dsacp")
+        "dtype": ("f32" if args.path == "fused" else "bf16" if args.path in ("fc2", "dsacp", "gemm")
                   else {torch.uint8: "u8", torch.bfloat16: "bf16"}.get(w.out_dtype, "f32")),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.description}" if args.path == "fused" else desc,
             "path": {"fused": "sp_reduce_add_rmsnorm", "gather": "sp_all_gather_unpad",
-                     "fc2": "sp_fc2_regroup", "dsacp": "sp_dsacp_heads_to_tokens"}[args.path],
+                     "fc2": "sp_fc2_regroup", "dsacp": "sp_dsacp_heads_to_tokens",
+                     "gemm": "sp_matmul_scatter"}[args.path],
             "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
             "shard_rows": w.shard_rows, "hidden": w.hidden,
             "quant": QUANT_NAMES[w.quant_mode] + (
                 (" e2m1" if w.fp4 else " e4m3") if w.quant_mode == QUANT_MX_BLOCK else ""),
             "deepstack": w.deepstack, "bias": w.bias,
-            "algorithmic_bytes": nbytes,
+            ("algorithmic_flops" if gemm else "algorithmic_bytes"): nbytes,
         },
-        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "shard_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
         "kernel_us": {
             "mean": round(avg_ms * 1000, 2),
@@ -359,17 +407,21 @@ def main():
             "p90": round(float(np.percentile(per_launch_ms, 90)) * 1000, 2),
         },
         "roofline": {
-            "bound": "hbm",
+            "bound": "mfma" if gemm else "hbm",
             "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak": peak,
+            "unit": "TFLOP/s" if gemm else "GB/s",
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0 and args.path == "fused":
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    if gemm:
+        result["context"] = {"hipblaslt_linear_us": round(library_gemm_us(x[0], x[1]), 2),
+                             "note": "torch's linear (hipBLASLt) on the same operands, "
+                                     "one [M, H] output, no scatter"}
     print(json.dumps(result), flush=True)
 
 

@@ -261,6 +261,49 @@ typedef struct {
 int sp_dsacp_heads_to_tokens(const sp_dsacp_problem* f, const void* const* attn,
                              void* const* out, void* stream);
 
+/* Problem descriptor of sp_matmul_scatter (host memory, read during the call only). */
+typedef struct {
+  int32_t tp;          /* ranks of the tensor-parallel group, 1 <= tp <= 64 */
+  int32_t rank;        /* the producing rank q, 0 <= rank < tp */
+  int64_t shard_rows;  /* S; x has M = tp*S token rows (padded), 0 <= M < 2^31 */
+  int64_t k;           /* K, this rank's slice of the input features, K % 8 == 0, 8 <= K <= 2^20 */
+  int64_t n;           /* N, output columns (the hidden size H), N % 8 == 0, 8 <= N <= 2^20 */
+  int32_t in_dtype;    /* SP_BF16 (x and w) */
+  int32_t out_dtype;   /* SP_BF16 | SP_F32: the partial dtype of the fused call */
+} sp_matmul_problem;
+
+/*
+ * sp_matmul_scatter -- the producer in front of the shard path: rank q's
+ * row-parallel GEMM with its ReduceScatter destinations (vLLM SP / AsyncTP
+ * / quantisation notes, §2, GEMM + ReduceScatter at a block's exit; o_proj
+ * split along K over the tp ranks: LongCat-Flash on Atlas A3, o_proj TP
+ * K-axis split).  It computes the unreduced partial
+ *
+ *   P[m][n] = sum over k of x[m][k] * w[n][k]      (fp32 accumulation)
+ *
+ * and writes token row m to rank r = m / S, row s = m - r*S, slot q of r's
+ * receive buffer:
+ *
+ *   dst[r][q][s][n] = P[m][n]   (rounded to out_dtype, nearest-even)
+ *
+ * so that dst[r], once every rank has written its slot, is exactly the
+ * partials[tp][S][N] argument of rank r's sp_reduce_add_rmsnorm.
+ *
+ *   p    problem descriptor (host)
+ *   x    device [M][K] bf16, this rank's K-slice of every token's input
+ *   w    device [N][K] bf16, this rank's K-slice of the weight (one row per
+ *        output column, the storage of a linear layer's weight)
+ *   dst  host array of tp device pointers, rank r's [tp][S][N] receive
+ *        buffer in out_dtype; only slot q (rows [q*S, (q+1)*S)) is written.
+ *        On one GPU these are local; on a node, peer-mapped buffers.
+ *
+ * Pointers 16-byte aligned; the written slots must not overlap x, w or each
+ * other.  M == 0 enqueues nothing.  Same error convention as
+ * sp_reduce_add_rmsnorm.
+ */
+int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, void* const* dst,
+                      void* stream);
+
 /*
  * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.
  * Same arguments (no stream); touches no device memory and makes no HIP

@@ -30,7 +30,8 @@ SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED
     0, -1, -2, -3, -4, -5, -6)
 
 EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_fc2_regroup",
-            "sp_dsacp_heads_to_tokens", "sp_shard_geometry", "sp_error_string", "sp_last_error")
+            "sp_dsacp_heads_to_tokens", "sp_matmul_scatter", "sp_shard_geometry",
+            "sp_error_string", "sp_last_error")
 SP_FLAG_VALID_ROWS_ONLY = 1
 
 
@@ -92,6 +93,18 @@ class sp_dsacp_problem(C.Structure):
     ]
 
 
+class sp_matmul_problem(C.Structure):
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("rank", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("k", C.c_int64),
+        ("n", C.c_int64),
+        ("in_dtype", C.c_int32),
+        ("out_dtype", C.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -121,6 +134,8 @@ def load(build_if_missing: bool = False):
     lib.sp_dsacp_heads_to_tokens.argtypes = [C.POINTER(sp_dsacp_problem), C.POINTER(vp),
                                              C.POINTER(vp), vp]
     lib.sp_dsacp_heads_to_tokens.restype = C.c_int
+    lib.sp_matmul_scatter.argtypes = [C.POINTER(sp_matmul_problem), vp, vp, C.POINTER(vp), vp]
+    lib.sp_matmul_scatter.restype = C.c_int
     lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
                                       C.POINTER(i64)]
     lib.sp_shard_geometry.restype = C.c_int
@@ -350,6 +365,31 @@ def sp_dsacp_heads_to_tokens(attn, outs, *, rank: int = -1, stream=None) -> None
     with torch.cuda.device(attn[0].device):
         _check(lib.sp_dsacp_heads_to_tokens(C.byref(f), src, dst,
                                             _stream_handle(attn[0].device, stream)))
+
+
+def sp_matmul_scatter(x, w, dsts, *, rank: int, stream=None) -> None:
+    """Rank `rank`'s row-parallel GEMM x w^T (x [tp*S, K] bf16, w [N, K] bf16)
+    written into slot `rank` of each destination's receive buffer dsts[r]
+    [tp, S, N] (bf16 or f32).  See include/sprms.h."""
+    lib = load()
+    tp = len(dsts)
+    M, K = x.shape
+    N = w.shape[0]
+    if M % tp or w.shape[1] != K:
+        raise ValueError("x must be [tp*S, K] and w [N, K]")
+    S = M // tp
+    for d in dsts:
+        if d.shape != (tp, S, N) or d.dtype != dsts[0].dtype:
+            raise ValueError("every receive buffer must be [tp, S, N] of one dtype")
+    _same_device(x, w, dsts)
+    p = sp_matmul_problem(tp=tp, rank=rank, shard_rows=S, k=K, n=N, in_dtype=_sp_dtype(x.dtype),
+                          out_dtype=_sp_dtype(dsts[0].dtype))
+    if _sp_dtype(w.dtype) != p.in_dtype:
+        raise ValueError("x and w must share a dtype")
+    dst = (C.c_void_p * tp)(*[_addr(d) for d in dsts])
+    with torch.cuda.device(x.device):
+        _check(lib.sp_matmul_scatter(C.byref(p), _addr(x), _addr(w), dst,
+                                     _stream_handle(x.device, stream)))
 
 
 def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,

@@ -11,8 +11,9 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-# the fused shard kernel and the layout kernels (gather, regroupings)
-SRCS = [os.path.join(PKG, "csrc", "sprms.hip"), os.path.join(PKG, "csrc", "layout.hip")]
+# the fused shard kernel, the layout kernels (gather, regroupings) and the
+# producer GEMM
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("sprms.hip", "layout.hip", "gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsprms.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,259 @@
+// gemm.hip -- the producer of the shard path: one rank's row-parallel GEMM
+// with its ReduceScatter destinations (include/sprms.h, sp_matmul_scatter).
+//
+// Rank q computes P = x w^T, x [M][K] and w [N][K] in bf16 (both operands
+// K-contiguous, the layout of a linear layer's weight), fp32 accumulation on
+// the matrix cores, and writes token row m straight into slot q of rank
+// m / S's [tp][S][N] receive buffer -- the buffer the fused reduce + add +
+// RMSNorm kernel consumes.  On one GPU the receive buffers are local; on a
+// node they would be peer-mapped and this epilogue is the "send each block as
+// soon as it is computed" half of a fused GEMM + ReduceScatter.
+//
+// Kernel design (gfx950, dense bf16: MFMA bound at the shapes of interest,
+// e.g. 2*65536*896*7168 flop against 1.07 GB at C4's shape, 785 flop/B, above
+// the 312 flop/B ridge of 2.5 PFLOP/s over 8 TB/s):
+//   * one workgroup (4 wavefronts) per 256 x 256 output tile; each wavefront
+//     owns 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
+//     accumulators per lane;
+//   * the weight tile is the MFMA's A operand and the token tile its B
+//     operand, so each lane's accumulators are 4-element runs of one token
+//     row's output columns: 8- or 16-byte stores in the epilogue;
+//   * K advances 64 at a time through two LDS stages (register-staged
+//     16-byte global loads issued before the current stage's MFMAs, written
+//     to the other stage after them: one barrier per step).  LDS rows are 64
+//     elements + 16 bytes of padding, so the 32 rows an MFMA operand read
+//     touches land on distinct banks in groups of 16;
+//   * tiles are ordered for the L2 of each XCD: workgroup b runs on XCD b % 8,
+//     each XCD gets a contiguous range of tile ids, and tile ids run over
+//     groups of 4 token bands x all column tiles, so the ~32 tiles resident
+//     on an XCD share their token bands and weight tiles;
+//   * tails: loads through per-tile buffer descriptors return 0 past the last
+//     row; the last K step masks 16-byte chunks at or past K (K % 8 == 0);
+//     stores are skipped past M and N.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "common.h"
+#include "sprms.h"
+
+namespace {
+
+using namespace sprms;
+
+constexpr int kBM = 256;                 // token rows per tile
+constexpr int kBN = 256;                 // output columns per tile
+constexpr int kBK = 64;                  // K per LDS stage
+constexpr int kThreads = 256;            // 4 wavefronts
+constexpr int kLdsRow = kBK * 2 + 16;    // bytes per LDS row (64 bf16 + padding)
+constexpr int kStageBytes = (kBM + kBN) * kLdsRow;
+constexpr int kChunksPerRow = kBK / 8;   // 16-byte chunks per row and stage
+constexpr int kRowsPerPass = kThreads / kChunksPerRow;   // 32
+constexpr int kPasses = kBM / kRowsPerPass;              // 8 rows per thread and operand
+constexpr int kGroupM = 4;               // token bands per tile group
+constexpr int kXcds = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct MArgs {
+  const char* x;            // [M][K] bf16
+  const char* w;            // [N][K] bf16
+  char* dst[kMaxTp];        // rank r's [tp][S][N] receive buffer
+  int64_t S;
+  int64_t slot;             // rank * S: first row of this rank's slot
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+};
+
+// tile id of workgroup b: XCD-contiguous ranges over a grouped order
+__device__ __forceinline__ void tile_of(const MArgs& a, int* tm, int* tn) {
+  const int total = a.tiles_m * a.tiles_n;
+  const int b = blockIdx.x;
+  const int x = b % kXcds, i = b / kXcds;
+  const int q = total / kXcds, rem = total % kXcds;
+  const int t = x * q + (x < rem ? x : rem) + i;
+  const int per_group = kGroupM * a.tiles_n;
+  const int g = t / per_group;
+  const int first = g * kGroupM;
+  const int gm = a.tiles_m - first < kGroupM ? a.tiles_m - first : kGroupM;
+  const int in = t - g * per_group;
+  *tm = first + in % gm;
+  *tn = in / gm;
+}
+
+template <int OUT>
+__global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  int tm, tn;
+  tile_of(a, &tm, &tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // per-tile descriptors: rows past M (N) read as zero
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+  const int rows_x = a.M - m0 < kBM ? a.M - m0 : kBM;
+  const int rows_w = a.N - n0 < kBN ? a.N - n0 : kBN;
+  const rsrc_t gx = row_rsrc(a.x + static_cast<int64_t>(m0) * row_bytes, static_cast<uint32_t>(rows_x) * row_bytes);
+  const rsrc_t gw = row_rsrc(a.w + static_cast<int64_t>(n0) * row_bytes, static_cast<uint32_t>(rows_w) * row_bytes);
+
+  // this thread's 16-byte chunk: column kc of rows r0 + 32 p
+  const int kc = tid % kChunksPerRow, r0 = tid / kChunksPerRow;
+  u32x4 rw[kPasses], rx[kPasses];
+  auto fetch = [&](int kb) {
+    const bool in_k = kb + kc * 8 < a.K;
+    const uint32_t col = static_cast<uint32_t>(kb + kc * 8) * 2u;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const uint32_t off = static_cast<uint32_t>(r0 + p * kRowsPerPass) * row_bytes + col;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      rw[p] = in_k ? __builtin_amdgcn_raw_buffer_load_b128(gw, off, 0, kCachedPolicy) : zero;
+      rx[p] = in_k ? __builtin_amdgcn_raw_buffer_load_b128(gx, off, 0, kCachedPolicy) : zero;
+    }
+  };
+  auto stash = [&](int stage) {
+    char* sw = smem + stage * kStageBytes;
+    char* sx = sw + kBN * kLdsRow;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int o = (r0 + p * kRowsPerPass) * kLdsRow + kc * 16;
+      *reinterpret_cast<u32x4*>(sw + o) = rw[p];
+      *reinterpret_cast<u32x4*>(sx + o) = rx[p];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = (a.K + kBK - 1) / kBK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  // operand rows of this lane inside a stage: row l%32 of each 32-row block,
+  // K half (l/32)*8
+  const int arow = wn * 128 + (lane & 31), brow = wm * 128 + (lane & 31);
+  const int khalf = (lane >> 5) * 16;  // bytes
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) fetch((kt + 1) * kBK);
+    const char* sw = smem + (kt & 1) * kStageBytes;
+    const char* sx = sw + kBN * kLdsRow;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(sw + (arow + i * 32) * kLdsRow + ks * 32 + khalf);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(sx + (brow + j * 32) * kLdsRow + ks * 32 + khalf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) stash((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue: acc[i][j][4g + c] is output (token m, column n + c) with
+  // m = m0 + wm*128 + 32j + l%32 and n = n0 + wn*128 + 32i + 8g + 4*(l/32)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + j * 32 + (lane & 31);
+    if (m >= a.M) continue;
+    const int64_t r = m / a.S;
+    const int64_t s = m - r * a.S;
+    char* row = a.dst[r] + (a.slot + s) * static_cast<int64_t>(a.N) * (OUT == SP_F32 ? 4 : 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+        if (n >= a.N) continue;
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if constexpr (OUT == SP_F32) {
+          const f32x4 v = {v0, v1, v2, v3};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(row + static_cast<int64_t>(n) * 4));
+        } else {
+          const f32x2 lo = {v0, v1}, hi = {v2, v3};
+          const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                           __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(row + static_cast<int64_t>(n) * 2));
+        }
+      }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, void* const* dst,
+                      void* stream) {
+  if (!p) return fail(SP_ERR_NULL, "matmul descriptor is NULL");
+  const int tp = p->tp;
+  if (tp < 1 || tp > kMaxTp) return fail(SP_ERR_SHAPE, "tp=%d outside [1, %d]", tp, kMaxTp);
+  if (p->rank < 0 || p->rank >= tp) return fail(SP_ERR_SHAPE, "rank=%d outside [0, %d)", p->rank, tp);
+  if (p->in_dtype != SP_BF16) return fail(SP_ERR_DTYPE, "in_dtype=%d: only SP_BF16 inputs", p->in_dtype);
+  if (p->out_dtype != SP_BF16 && p->out_dtype != SP_F32)
+    return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_BF16 or SP_F32", p->out_dtype);
+  const int64_t S = p->shard_rows, K = p->k, N = p->n;
+  const int64_t M = S * tp;
+  if (S < 0 || M > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
+  if (K < 8 || K % 8 != 0 || K > (1 << 20))
+    return fail(SP_ERR_SHAPE, "k=%lld must be a multiple of 8 in [8, 2^20]", (long long)K);
+  if (N < 8 || N % 8 != 0 || N > (1 << 20))
+    return fail(SP_ERR_SHAPE, "n=%lld must be a multiple of 8 in [8, 2^20]", (long long)N);
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (tiles > INT32_MAX) return fail(SP_ERR_SHAPE, "too many tiles for one grid");
+  if (M == 0) return SP_OK;
+  if (!x || !w || !dst) return fail(SP_ERR_NULL, "x, w and dst must be non-NULL");
+  if (misaligned(x) || misaligned(w)) return fail(SP_ERR_ALIGN, "x and w must be 16-byte aligned");
+  const size_t e = p->out_dtype == SP_F32 ? 4 : 2;
+  const size_t slot_n = static_cast<size_t>(S) * N * e;  // bytes this rank writes per destination
+  const size_t x_n = static_cast<size_t>(M) * K * 2, w_n = static_cast<size_t>(N) * K * 2;
+  MArgs ma;
+  memset(&ma, 0, sizeof ma);
+  for (int r = 0; r < tp; ++r) {
+    if (!dst[r]) return fail(SP_ERR_NULL, "dst[%d] is NULL", r);
+    if (misaligned(dst[r])) return fail(SP_ERR_ALIGN, "dst[%d] is not 16-byte aligned", r);
+    const char* slot = static_cast<const char*>(dst[r]) + static_cast<size_t>(p->rank) * slot_n;
+    if (overlap(slot, slot_n, x, x_n) || overlap(slot, slot_n, w, w_n))
+      return fail(SP_ERR_SHAPE, "dst[%d] slot %d overlaps x or w", r, p->rank);
+    for (int r2 = 0; r2 < r; ++r2) {
+      const char* other = static_cast<const char*>(dst[r2]) + static_cast<size_t>(p->rank) * slot_n;
+      if (overlap(slot, slot_n, other, slot_n))
+        return fail(SP_ERR_SHAPE, "dst[%d] and dst[%d] slots overlap", r, r2);
+    }
+    ma.dst[r] = static_cast<char*>(dst[r]);
+  }
+  ma.x = static_cast<const char*>(x);
+  ma.w = static_cast<const char*>(w);
+  ma.S = S;
+  ma.slot = static_cast<int64_t>(p->rank) * S;
+  ma.M = static_cast<int32_t>(M);
+  ma.N = static_cast<int32_t>(N);
+  ma.K = static_cast<int32_t>(K);
+  ma.tiles_m = static_cast<int32_t>((M + kBM - 1) / kBM);
+  ma.tiles_n = static_cast<int32_t>((N + kBN - 1) / kBN);
+  void* args[] = {&ma};
+  const void* fn = p->out_dtype == SP_F32 ? reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_F32>)
+                                          : reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_BF16>);
+  hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), args, 0,
+                                   static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(SP_ERR_HIP, "matmul launch failed: %s", hipGetErrorString(err));
+  return SP_OK;
+}
+
+}  // extern "C"

@@ -294,6 +294,49 @@ def test_fc2_regroup_empty_is_a_no_op():
     assert _fc2(N=0, Cc=2, src=[BASE + 4, BASE + GB, BASE + 2 * GB, BASE + 3 * GB])[0] == sp.SP_OK
 
 
+def _mm(tp=4, rank=1, S=64, K=896, N=1024, in_dtype=sp.SP_BF16, out_dtype=sp.SP_F32, x=BASE,
+        w=BASE + GB, dst=None):
+    import ctypes as C
+    lib = sp.load()
+    p = sp.sp_matmul_problem(tp=tp, rank=rank, shard_rows=S, k=K, n=N, in_dtype=in_dtype,
+                             out_dtype=out_dtype)
+    dst = dst if dst is not None else [BASE + (2 + r) * GB for r in range(max(tp, 1))]
+    d = (C.c_void_p * len(dst))(*dst)
+    return lib.sp_matmul_scatter(C.byref(p), x, w, d, None), sp.sp_last_error()
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(tp=0), sp.SP_ERR_SHAPE),
+    (dict(tp=65, dst=[BASE + (2 + r) * GB for r in range(65)]), sp.SP_ERR_SHAPE),
+    (dict(rank=4), sp.SP_ERR_SHAPE),
+    (dict(rank=-1), sp.SP_ERR_SHAPE),
+    (dict(in_dtype=sp.SP_F32), sp.SP_ERR_DTYPE),
+    (dict(out_dtype=sp.SP_FP8_E4M3), sp.SP_ERR_DTYPE),
+    (dict(S=-1), sp.SP_ERR_SHAPE),
+    (dict(S=1 << 29), sp.SP_ERR_SHAPE),                   # tp*S = 2^31
+    (dict(K=4), sp.SP_ERR_SHAPE),
+    (dict(K=900), sp.SP_ERR_SHAPE),
+    (dict(K=(1 << 20) + 8), sp.SP_ERR_SHAPE),
+    (dict(N=1028), sp.SP_ERR_SHAPE),
+    (dict(x=0), sp.SP_ERR_NULL),
+    (dict(w=0), sp.SP_ERR_NULL),
+    (dict(dst=[BASE + 2 * GB, 0, BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_NULL),
+    (dict(x=BASE + 8), sp.SP_ERR_ALIGN),
+    (dict(dst=[BASE + 2 * GB, BASE + 3 * GB + 4, BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_ALIGN),
+    # slot 1 of dst[0] (bytes [64*1024*4, 2*64*1024*4)) on top of x
+    (dict(dst=[BASE - 64 * 1024 * 4, BASE + 3 * GB, BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_SHAPE),
+    # slots of two destinations overlap
+    (dict(dst=[BASE + 2 * GB, BASE + 2 * GB + 1024, BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_SHAPE),
+])
+def test_matmul_scatter_rejects_invalid_problems(case, expect):
+    status, msg = _mm(**case)
+    assert status == expect, msg
+
+
+def test_matmul_scatter_empty_is_a_no_op():
+    assert _mm(S=0, x=0, w=0)[0] == sp.SP_OK
+
+
 def test_null_descriptor():
     lib = sp.load()
     assert lib.sp_validate(None, None, None, None, None, 0.0, 0, None, None, None) == sp.SP_ERR_NULL

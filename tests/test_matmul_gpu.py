@@ -1,0 +1,210 @@
+"""The producer GEMM (sp_matmul_scatter) against the oracle, and the chain
+producer -> fused shard kernel against the oracle's chain (vLLM SP /
+AsyncTP / quantisation notes, §2: GEMM + ReduceScatter at a block's exit).
+
+Tolerance: the GPU sums K bf16 products in fp32 on the matrix cores; the
+oracle sums them exactly (fp64) and rounds once.  With A = sum_k |x_k w_k|,
+the fp32 sum differs from the exact one by at most (K + 2) 2^-24 A; the
+oracle's f32 value adds 2^-24 of itself.  A bf16 output must lie between the
+bf16 roundings of the interval's ends (rounding is monotone)."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import reduce_add_rmsnorm_amd as sp
+from helpers import bf16_bits_to_f64, bf16_round, to_host, within_rounding
+from parity import run_case
+from reduce_add_rmsnorm_amd.inputs import QUANT_DYNAMIC_TOKEN, QUANT_NONE, WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 0xA5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sp.load()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _operands(M, K, N, dev, seed, integers=False):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    if integers:
+        x = torch.randint(-3, 4, (M, K), generator=g, device=dev).to(torch.bfloat16)
+        w = torch.randint(-3, 4, (N, K), generator=g, device=dev).to(torch.bfloat16)
+    else:
+        x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        w = (torch.randn((N, K), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    return x, w
+
+
+def _receive_buffers(tp, S, N, dtype, dev):
+    bufs = []
+    for _ in range(tp):
+        b = torch.empty((tp, S, N), dtype=dtype, device=dev)
+        b.view(torch.uint8).fill_(CANARY)
+        bufs.append(b)
+    return bufs
+
+
+def _check(x, w, dsts, rank, rows=None):
+    """Rows m (default all) of rank's partial, read back from slot `rank` of
+    their destinations, against the oracle."""
+    tp = len(dsts)
+    M, K = x.shape
+    N = w.shape[0]
+    S = M // tp
+    f32 = dsts[0].dtype == torch.float32
+    rows = np.arange(M) if rows is None else np.asarray(sorted(set(int(m) for m in rows)))
+    hx, hw = to_host(x), to_host(w)
+    ref32 = oracle.matmul_scatter(hx, hw, tp=tp, rank=rank, out_dtype=oracle.ORC_F32, rows=rows)
+    ref16 = None if f32 else oracle.matmul_scatter(hx, hw, tp=tp, rank=rank,
+                                                   out_dtype=oracle.ORC_BF16, rows=rows)
+    ax = np.abs(bf16_bits_to_f64(hx[rows]))
+    aw = np.abs(bf16_bits_to_f64(hw))
+    A = ax @ aw.T                                   # sum_k |x_k w_k|, for the bound only
+    exact_eq = []
+    for i, m in enumerate(rows):
+        r, s = divmod(int(m), S)
+        want = ref32[r][rank][s].astype(np.float64)
+        E = (K + 2) * 2.0 ** -24 * A[i] + 2.0 ** -24 * np.abs(want)
+        got_t = dsts[r][rank, s]
+        if f32:
+            got = got_t.cpu().numpy().astype(np.float64)
+            assert (np.abs(got - want) <= E).all(), f"row {m}: f32 partial outside the bound"
+        else:
+            bits = to_host(got_t)
+            got = bf16_bits_to_f64(bits)
+            ok = within_rounding(got, want - E, want + E, bf16_round)
+            assert ok.all(), f"row {m}: bf16 partial outside the bound at {np.argwhere(~ok)[:4].tolist()}"
+            exact_eq.append((bits == ref16[r][rank][s]).mean())
+    if exact_eq:
+        assert np.mean(exact_eq) >= 0.99, f"only {np.mean(exact_eq):.4f} of bf16 partials equal the oracle's"
+
+
+def _slots_untouched(dsts, rank):
+    for r, d in enumerate(dsts):
+        b = d.view(torch.uint8)
+        for q in range(d.shape[0]):
+            if q != rank:
+                assert bool((b[q] == CANARY).all()), f"dst[{r}] slot {q} was written"
+
+
+@pytest.mark.parametrize("tp,S,K,N,dtype", [
+    (2, 300, 136, 520, torch.float32),   # 3 x 3 tiles, ragged M, N and a K tail of 8
+    (2, 300, 136, 520, torch.bfloat16),
+    (4, 64, 64, 256, torch.bfloat16),    # exactly one tile
+    (1, 5, 8, 8, torch.float32),         # smallest
+    (8, 33, 896, 1024, torch.bfloat16),  # K of one rank at hidden 7168 over 8 ranks
+    (3, 100, 1288, 264, torch.float32),  # long K with a tail, N just past a tile
+])
+def test_matmul_scatter_matches_oracle(dev, tp, S, K, N, dtype):
+    M = tp * S
+    say(f"matmul_scatter tp={tp} S={S} K={K} N={N} {dtype}")
+    x, w = _operands(M, K, N, dev, seed=M + K + N)
+    for rank in sorted({0, tp - 1}):
+        dsts = _receive_buffers(tp, S, N, dtype, dev)
+        sp.sp_matmul_scatter(x, w, dsts, rank=rank)
+        torch.cuda.synchronize()
+        _check(x, w, dsts, rank)
+        _slots_untouched(dsts, rank)
+
+
+def test_matmul_scatter_integer_inputs_are_exact(dev):
+    tp, S, K, N = 4, 130, 320, 384
+    x, w = _operands(tp * S, K, N, dev, seed=3, integers=True)
+    for dtype, od in ((torch.float32, oracle.ORC_F32), (torch.bfloat16, oracle.ORC_BF16)):
+        dsts = _receive_buffers(tp, S, N, dtype, dev)
+        sp.sp_matmul_scatter(x, w, dsts, rank=2)
+        torch.cuda.synchronize()
+        ref = oracle.matmul_scatter(to_host(x), to_host(w), tp=tp, rank=2, out_dtype=od)
+        for r in range(tp):
+            np.testing.assert_array_equal(to_host(dsts[r][2]).view(np.uint8), ref[r][2].view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_matmul_scatter_full_size_sampled_rows(dev, name):
+    # the benchmark's shape and launch: M = T_pad tokens, K = H / tp, N = H,
+    # bf16 partials, the timed rank
+    w_ = WORKLOADS[name]
+    tp, S, H = w_.tp, w_.shard_rows, w_.hidden
+    M, K = tp * S, H // tp
+    say(f"matmul_scatter {name}: M={M} K={K} N={H} rank {w_.rank}, sampled rows")
+    x, w = _operands(M, K, H, dev, seed=11)
+    dsts = [torch.empty((tp, S, H), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+    sp.sp_matmul_scatter(x, w, dsts, rank=w_.rank)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = [0, 1, 255, 256, 257, S - 1, S, M - 256, M - 1] + list(rng.integers(0, M, 24))
+    _check(x, w, dsts, w_.rank, rows=rows)
+
+
+@pytest.mark.parametrize("quant", [QUANT_NONE, QUANT_DYNAMIC_TOKEN])
+def test_producer_then_fused_kernel(dev, quant):
+    """Every rank's GEMM writes its slot; each rank's receive buffer then goes
+    through the fused kernel.  Integer operands: the GPU's receive buffers
+    equal the oracle's bit for bit, and the fused outputs match the oracle's
+    fused call on the oracle's buffers."""
+    tp, S, Kr, N = 4, 96, 128, 1024
+    T = tp * S - 10
+    say(f"producer -> fused: tp={tp} S={S} K/rank={Kr} N={N} T={T} quant={quant}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    X = torch.randint(-2, 3, (tp * S, tp * Kr), generator=g, device=dev).to(torch.bfloat16)
+    W = torch.randint(-2, 3, (N, tp * Kr), generator=g, device=dev).to(torch.bfloat16)
+    resid = torch.randint(-4, 5, (tp * S, N), generator=g, device=dev).to(torch.bfloat16)
+    wt = (torch.randn((N,), generator=g, device=dev) * 0.1 + 1).to(torch.bfloat16)
+    dsts = [torch.empty((tp, S, N), dtype=torch.float32, device=dev) for _ in range(tp)]
+    ref = None
+    for q in range(tp):
+        xq = X[:, q * Kr:(q + 1) * Kr].contiguous()
+        wq = W[:, q * Kr:(q + 1) * Kr].contiguous()
+        sp.sp_matmul_scatter(xq, wq, dsts, rank=q)
+        ref = oracle.matmul_scatter(to_host(xq), to_host(wq), tp=tp, rank=q, dst=ref)
+    torch.cuda.synchronize()
+    odt = torch.bfloat16 if quant == QUANT_NONE else torch.uint8
+    w = dataclasses.replace(WORKLOADS["C2"], tp=tp, num_tokens=T, num_tokens_pad=tp * S, hidden=N,
+                            partial_dtype=torch.float32, quant_mode=quant, out_dtype=odt,
+                            residual_replicated=True, deepstack=False, bias=False)
+    for r in range(tp):
+        np.testing.assert_array_equal(dsts[r].cpu().numpy(), ref[r])
+        say(f"fused call of rank {r} on its receive buffer")
+        run_case(w, r, dev=dev, inputs={"partials": torch.from_numpy(ref[r]).to(dev),
+                                        "residual": resid, "weight": wt, "bias": None,
+                                        "deepstack": None})
+        # and the kernel reading the producer's buffer directly gives the same bytes
+        outs = []
+        for parts in (dsts[r], torch.from_numpy(ref[r]).to(dev)):
+            out = torch.empty((S, N), dtype=odt, device=dev)
+            ro = torch.empty((S, N), dtype=torch.bfloat16, device=dev)
+            sc = torch.empty((S,), device=dev) if quant == QUANT_DYNAMIC_TOKEN else None
+            sp.sp_reduce_add_rmsnorm(parts, resid, wt, None, 1e-6, quant, None, out, sc,
+                                     tp_rank=r, num_tokens=T, residual_out=ro)
+            outs.append((out, ro))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0].view(torch.uint8), outs[1][0].view(torch.uint8))
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+def test_matmul_scatter_rejects_bad_calls(dev):
+    x, w = _operands(8, 16, 16, dev, seed=1)
+    dsts = [torch.empty((2, 4, 16), dtype=torch.float32, device=dev) for _ in range(2)]
+    with pytest.raises(sp.SprmsError) as e:
+        sp.sp_matmul_scatter(x, w, dsts, rank=2)
+    assert e.value.status == sp.SP_ERR_SHAPE
+    with pytest.raises(sp.SprmsError) as e:
+        sp.sp_matmul_scatter(x, w, [dsts[0], dsts[0]], rank=0)   # slots overlap
+    assert e.value.status == sp.SP_ERR_SHAPE
+    with pytest.raises(ValueError):
+        sp.sp_matmul_scatter(x, w.cpu(), dsts, rank=0)
