@@ -12,24 +12,30 @@
 // Kernel design (gfx950, dense bf16: MFMA bound at the shapes of interest,
 // e.g. 2*65536*896*7168 flop against 1.07 GB at C4's shape, 785 flop/B, above
 // the 312 flop/B ridge of 2.5 PFLOP/s over 8 TB/s):
-//   * one workgroup (4 wavefronts) per 256 x 256 output tile; each wavefront
-//     owns 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, 256 fp32
-//     accumulators per lane;
+//   * one workgroup of 8 wavefronts per 256 x 256 output tile, two
+//     wavefronts per SIMD so that one issues MFMAs while the other waits on
+//     LDS or a barrier; each wavefront owns 128 columns x 64 tokens as 4 x 2
+//     blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane);
 //   * the weight tile is the MFMA's A operand and the token tile its B
 //     operand, so each lane's accumulators are 4-element runs of one token
-//     row's output columns: 8- or 16-byte stores in the epilogue;
-//   * K advances 64 at a time through two LDS stages (register-staged
-//     16-byte global loads issued before the current stage's MFMAs, written
-//     to the other stage after them: one barrier per step).  LDS rows are 64
-//     elements + 16 bytes of padding, so the 32 rows an MFMA operand read
-//     touches land on distinct banks in groups of 16;
+//     row's output columns;
+//   * K advances 64 at a time through two LDS stages filled by buffer loads
+//     that write LDS directly (16 bytes per lane, no staging registers): the
+//     loads of step k+1 are issued before step k's MFMAs and waited for
+//     before the barrier that ends the step.  LDS rows are 128 bytes with
+//     their 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 rows an
+//     MFMA operand read touches per 16 lanes land on distinct banks;
+//   * the epilogue stages the rounded tile in LDS and writes each token row
+//     as 512 contiguous bytes (16 per lane): written from the accumulator
+//     layout directly, every 8-byte piece became its own DRAM write, 4x the
+//     output bytes;
 //   * tiles are ordered for the L2 of each XCD: workgroup b runs on XCD b % 8,
 //     each XCD gets a contiguous range of tile ids, and tile ids run over
 //     groups of 4 token bands x all column tiles, so the ~32 tiles resident
 //     on an XCD share their token bands and weight tiles;
 //   * tails: loads through per-tile buffer descriptors return 0 past the last
-//     row; the last K step masks 16-byte chunks at or past K (K % 8 == 0);
-//     stores are skipped past M and N.
+//     row; chunks at or past K (K % 8 == 0) are given an offset past the
+//     descriptor, which also reads 0; stores are skipped past M and N.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -45,18 +51,22 @@ using namespace sprms;
 constexpr int kBM = 256;                 // token rows per tile
 constexpr int kBN = 256;                 // output columns per tile
 constexpr int kBK = 64;                  // K per LDS stage
-constexpr int kThreads = 256;            // 4 wavefronts
-constexpr int kLdsRow = kBK * 2 + 16;    // bytes per LDS row (64 bf16 + padding)
-constexpr int kStageBytes = (kBM + kBN) * kLdsRow;
-constexpr int kChunksPerRow = kBK / 8;   // 16-byte chunks per row and stage
-constexpr int kRowsPerPass = kThreads / kChunksPerRow;   // 32
-constexpr int kPasses = kBM / kRowsPerPass;              // 8 rows per thread and operand
+constexpr int kThreads = 512;            // 8 wavefronts
+constexpr int kOpBytes = kBM * kBK * 2;  // one operand of one stage: 256 rows x 128 bytes
+constexpr int kStageBytes = 2 * kOpBytes;
+// epilogue staging: a bf16 tile (256 rows of 512 bytes + 16 of padding) at
+// once, an f32 tile in two passes of 128 rows of 1 KiB + 16
+constexpr int kOutRowsF32 = 128;
+constexpr int out_row_bytes(int esz) { return kBN * esz + 16; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kSmemBytes = cmax(2 * kStageBytes, cmax(kBM * out_row_bytes(2), kOutRowsF32 * out_row_bytes(4)));
 constexpr int kGroupM = 4;               // token bands per tile group
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct MArgs {
   const char* x;            // [M][K] bf16
@@ -84,15 +94,18 @@ __device__ __forceinline__ void tile_of(const MArgs& a, int* tm, int* tn) {
   *tn = in / gm;
 }
 
+// physical 16-byte chunk of logical chunk c in LDS row `row`
+__device__ __forceinline__ int swizzle(int row, int c) { return c ^ ((row >> 1) & 7); }
+
 template <int OUT>
 __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   int tm, tn;
   tile_of(a, &tm, &tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;  // tokens [wm*64, +64), columns [wn*128, +128)
 
   // per-tile descriptors: rows past M (N) read as zero
   const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
@@ -101,97 +114,114 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   const rsrc_t gx = row_rsrc(a.x + static_cast<int64_t>(m0) * row_bytes, static_cast<uint32_t>(rows_x) * row_bytes);
   const rsrc_t gw = row_rsrc(a.w + static_cast<int64_t>(n0) * row_bytes, static_cast<uint32_t>(rows_w) * row_bytes);
 
-  // this thread's 16-byte chunk: column kc of rows r0 + 32 p
-  const int kc = tid % kChunksPerRow, r0 = tid / kChunksPerRow;
-  u32x4 rw[kPasses], rx[kPasses];
-  auto fetch = [&](int kb) {
-    const bool in_k = kb + kc * 8 < a.K;
-    const uint32_t col = static_cast<uint32_t>(kb + kc * 8) * 2u;
+  // One load instruction of a wavefront fills 1 KiB of LDS: 8 rows x 128
+  // bytes, lane l at byte 16*l, i.e. row l >> 3, physical chunk l & 7; the
+  // lane fetches the logical chunk that the swizzle puts there.
+  const int grow = lane >> 3, pchunk = lane & 7;
+  auto issue = [&](int stage, int kb) {
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const uint32_t off = static_cast<uint32_t>(r0 + p * kRowsPerPass) * row_bytes + col;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      rw[p] = in_k ? __builtin_amdgcn_raw_buffer_load_b128(gw, off, 0, kCachedPolicy) : zero;
-      rx[p] = in_k ? __builtin_amdgcn_raw_buffer_load_b128(gx, off, 0, kCachedPolicy) : zero;
-    }
-  };
-  auto stash = [&](int stage) {
-    char* sw = smem + stage * kStageBytes;
-    char* sx = sw + kBN * kLdsRow;
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int o = (r0 + p * kRowsPerPass) * kLdsRow + kc * 16;
-      *reinterpret_cast<u32x4*>(sw + o) = rw[p];
-      *reinterpret_cast<u32x4*>(sx + o) = rx[p];
+    for (int t = 0; t < kBM / 8 / (kThreads / 64); ++t) {
+      const int g = wave + (kThreads / 64) * t;  // group of 8 rows
+      const int row = g * 8 + grow;
+      const int k = kb + swizzle(row, pchunk) * 8;
+      const uint32_t oob = (static_cast<uint32_t>(k - a.K) >> 31) ? 0u : 0x80000000u;
+      const uint32_t off = (static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(k) * 2u) | oob;
+      char* base = smem + stage * kStageBytes + g * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gw, (lds_void*)base, 16, off, 0, 0, kCachedPolicy);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gx, (lds_void*)(base + kOpBytes), 16, off, 0, 0, kCachedPolicy);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (a.K + kBK - 1) / kBK;
-  fetch(0);
-  stash(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // operand rows of this lane inside a stage: row l%32 of each 32-row block,
-  // K half (l/32)*8
-  const int arow = wn * 128 + (lane & 31), brow = wm * 128 + (lane & 31);
-  const int khalf = (lane >> 5) * 16;  // bytes
+  // operand rows of this lane: row l%32 of each 32-row block, K half l/32
+  const int arow = wn * 128 + (lane & 31), brow = wm * 64 + (lane & 31);
+  const int khalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) fetch((kt + 1) * kBK);
+    // the next step's loads (past K on the last step: zeros into the idle stage)
+    issue((kt + 1) & 1, (kt + 1) * kBK);
     const char* sw = smem + (kt & 1) * kStageBytes;
-    const char* sx = sw + kBN * kLdsRow;
+    const char* sx = sw + kOpBytes;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 fa[4], fb[4];
+      const int c = ks * 2 + khalf;
+      bf16x8 fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = arow + i * 32;
+        fa[i] = *reinterpret_cast<const bf16x8*>(sw + r * 128 + swizzle(r, c) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = brow + j * 32;
+        fb[j] = *reinterpret_cast<const bf16x8*>(sx + r * 128 + swizzle(r, c) * 16);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(sw + (arow + i * 32) * kLdsRow + ks * 32 + khalf);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(sx + (brow + j * 32) * kLdsRow + ks * 32 + khalf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) stash((kt + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the next stage have landed
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][4g + c] is output (token m, column n + c) with
-  // m = m0 + wm*128 + 32j + l%32 and n = n0 + wn*128 + 32i + 8g + 4*(l/32)
+  // Epilogue: acc[i][j][4g + c] is output (token ml, column nl + c) with
+  // ml = wm*64 + 32j + l%32, nl = wn*128 + 32i + 8g + 4*(l/32).  The rounded
+  // tile goes through LDS (bf16: all 256 rows at once; f32: 128 rows per
+  // pass), then each token row leaves as 16 bytes per lane.
+  constexpr int esz = OUT == SP_F32 ? 4 : 2;
+  constexpr int rows_per_pass = OUT == SP_F32 ? kOutRowsF32 : kBM;
+  constexpr int lanes_per_row = kBN * esz / 16;  // 32 (bf16) or 64 (f32)
+  constexpr int out_row = out_row_bytes(esz);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + (lane & 31);
-    if (m >= a.M) continue;
-    const int64_t r = m / a.S;
-    const int64_t s = m - r * a.S;
-    char* row = a.dst[r] + (a.slot + s) * static_cast<int64_t>(a.N) * (OUT == SP_F32 ? 4 : 2);
+  for (int pass = 0; pass < kBM / rows_per_pass; ++pass) {
+    if (pass > 0) __syncthreads();  // the previous pass's rows have been read
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) {
+      const int ml = wm * 64 + j * 32 + (lane & 31) - pass * rows_per_pass;
+      if (ml < 0 || ml >= rows_per_pass) continue;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-        if (n >= a.N) continue;
-        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (OUT == SP_F32) {
-          const f32x4 v = {v0, v1, v2, v3};
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(row + static_cast<int64_t>(n) * 4));
-        } else {
-          const f32x2 lo = {v0, v1}, hi = {v2, v3};
-          const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
-                           __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(row + static_cast<int64_t>(n) * 2));
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          char* dst = smem + ml * out_row + nl * esz;
+          if constexpr (OUT == SP_F32) {
+            const f32x4 v = {v0, v1, v2, v3};
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+            const f32x2 lo = {v0, v1}, hi = {v2, v3};
+            const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+            *reinterpret_cast<u32x2*>(dst) = v;
+          }
         }
-      }
+    }
+    __syncthreads();
+    const int col = (tid % lanes_per_row) * 16;  // byte offset in the row segment
+    const bool col_ok = n0 + col / esz < a.N;    // N % 8 == 0: a 16-byte piece is all in or all out
+    for (int rr = tid / lanes_per_row; rr < rows_per_pass; rr += kThreads / lanes_per_row) {
+      const int m = m0 + pass * rows_per_pass + rr;
+      if (m >= a.M || !col_ok) continue;
+      const uint32_t r = static_cast<uint32_t>(m) / static_cast<uint32_t>(a.S);
+      const int64_t s = m - static_cast<int64_t>(r) * a.S;
+      char* row = a.dst[r] + ((a.slot + s) * static_cast<int64_t>(a.N) + n0) * esz;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rr * out_row + col);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(row + col));
+    }
   }
 }
 
