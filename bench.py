@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 # layout kernels (gather, regroupings)
 _CSRC = os.path.join(ROOT, "reduce_add_rmsnorm_amd", "csrc")
 KERNEL_SRCS = {"fused": [os.path.join(_CSRC, f) for f in ("sprms.hip", "common.h")],
-               "layout": [os.path.join(_CSRC, f) for f in ("layout.hip", "common.h")]}
+               "layout": [os.path.join(_CSRC, f) for f in ("layout.hip", "common.h")],
+               "gemm": [os.path.join(_CSRC, f) for f in ("gemm.hip", "common.h")]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
 QUANT_NAMES = {0: "none (bf16 out)", 1: "static per-tensor e4m3", 2: "dynamic per-token e4m3",
                4: "block-scaled (32-element E8M0 scales)"}
@@ -367,7 +368,7 @@ def main():
     achieved = nbytes / (avg_ms / 1000.0) / scale
     traffic = measured_traffic(w.name if args.path == "fused" and not args.quant else
                                f"{w.name}-{args.path}-{args.quant}",
-                               "fused" if args.path == "fused" else "layout")
+                               {"fused": "fused", "gemm": "gemm"}.get(args.path, "layout"))
 
     result = {
         "metric": METRIC if args.path == "fused" else
@@ -397,6 +398,10 @@ def main():
                 (" e2m1" if w.fp4 else " e4m3") if w.quant_mode == QUANT_MX_BLOCK else ""),
             "deepstack": w.deepstack, "bias": w.bias,
             ("algorithmic_flops" if gemm else "algorithmic_bytes"): nbytes,
+            # the GEMM moves x, w and its output once each
+            **({"algorithmic_bytes": 2 * (w.num_tokens_pad * (w.hidden // w.tp)
+                                          + w.hidden * (w.hidden // w.tp) + w.num_tokens_pad * w.hidden)}
+               if gemm else {}),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "shard_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
