@@ -31,5 +31,6 @@ from .oracle import (  # noqa: F401
     fc2_regroup,
     matmul_scatter,
     reduce_add_rmsnorm,
+    scaled_matmul_scatter,
     shard_geometry,
 )

@@ -92,6 +92,9 @@ def _load():
     lib.orc_matmul_scatter.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i64, vp,
                                        C.POINTER(vp)]
     lib.orc_matmul_scatter.restype = C.c_int
+    lib.orc_scaled_matmul_scatter.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i64, vp, vp, i64,
+                                              i64, vp, C.POINTER(vp)]
+    lib.orc_scaled_matmul_scatter.restype = C.c_int
     lib.orc_e2m1_from_double.argtypes = [C.c_double]
     lib.orc_e2m1_from_double.restype = C.c_uint8
     lib.orc_e2m1_to_double.argtypes = [C.c_uint8]
@@ -326,4 +329,32 @@ def matmul_scatter(x, w, *, tp, rank, out_dtype=ORC_F32, rows=None, dst=None):
                                 0 if r is None else len(r), None if r is None else _ptr(r), dp)
     if rc != 0:
         raise OracleError(f"orc_matmul_scatter failed: {rc}")
+    return dst
+
+
+def scaled_matmul_scatter(x, x_scale, w, w_scale, *, tp, rank, out_dtype=ORC_F32, rows=None,
+                          dst=None):
+    """FP8 producer: x [tp*S, K] and w [N, K] e4m3 codes (uint8), x_scale
+    [1] or [tp*S] and w_scale [1] or [N] float32; P = (x w^T) x_scale w_scale
+    written into slot `rank` of the tp receive buffers [tp][S][N]."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xs = np.ascontiguousarray(x_scale, dtype=np.float32).reshape(-1)
+    ws = np.ascontiguousarray(w_scale, dtype=np.float32).reshape(-1)
+    M, K = x.shape
+    N = w.shape[0]
+    if M % tp or w.shape[1] != K:
+        raise OracleError("x must be [tp*S, K] and w [N, K]")
+    S = M // tp
+    dt = np.float32 if out_dtype == ORC_F32 else np.uint16
+    if dst is None:
+        dst = [np.zeros((tp, S, N), dtype=dt) for _ in range(tp)]
+    dp = (C.c_void_p * tp)(*[d.ctypes.data for d in dst])
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    rc = lib.orc_scaled_matmul_scatter(tp, rank, S, K, N, out_dtype, _ptr(x), _ptr(xs), xs.size,
+                                       _ptr(w), _ptr(ws), ws.size, 0 if r is None else len(r),
+                                       None if r is None else _ptr(r), dp)
+    if rc != 0:
+        raise OracleError(f"orc_scaled_matmul_scatter failed: {rc}")
     return dst

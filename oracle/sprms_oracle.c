@@ -542,3 +542,43 @@ int orc_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N
   }
   return ORC_OK;
 }
+
+/* The FP8 form of the producer ([SPquant] §四: after SP the row-parallel
+ * GEMM is an FP8 GEMM with its scales, fused with the ReduceScatter): x and
+ * w hold OCP e4m3 codes; x_scale has 1 (per tensor) or M (per token) fp32
+ * entries, w_scale 1 (per tensor) or N (per output column), and
+ *   P[m][n] = (sum over k of dec(x[m][k]) * dec(w[n][k])) * x_scale[m] * w_scale[n]
+ * with the dot product exact in fp64 (e4m3 products are exact) and one
+ * rounding to out_dtype.  Scattered like orc_matmul_scatter. */
+int orc_scaled_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N,
+                              int32_t out_dtype, const uint8_t* x, const float* x_scale,
+                              int64_t x_scale_rows, const uint8_t* w, const float* w_scale,
+                              int64_t w_scale_rows, int64_t n_rows, const int64_t* rows,
+                              void* const* dst) {
+  if (tp < 1 || rank < 0 || rank >= tp || S < 0 || K < 1 || N < 1) return ORC_ERR_SHAPE;
+  if (out_dtype != ORC_BF16 && out_dtype != ORC_F32) return ORC_ERR_DTYPE;
+  const int64_t M = (int64_t)tp * S;
+  if (x_scale_rows != 1 && x_scale_rows != M) return ORC_ERR_SHAPE;
+  if (w_scale_rows != 1 && w_scale_rows != N) return ORC_ERR_SHAPE;
+  const int64_t count = rows ? n_rows : M;
+  if (count == 0) return ORC_OK;
+  if (!x || !w || !x_scale || !w_scale || !dst) return ORC_ERR_NULL;
+  for (int r = 0; r < tp; ++r)
+    if (!dst[r]) return ORC_ERR_NULL;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows && (rows[i] < 0 || rows[i] >= M)) return ORC_ERR_SHAPE;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t m = rows ? rows[i] : i;
+    const int64_t r = m / S;     /* destination rank of this token */
+    const int64_t s = m - r * S; /* its row in that rank's shard */
+    const double sx = (double)x_scale[x_scale_rows == 1 ? 0 : m];
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += orc_e4m3_to_double(x[m * K + k]) * orc_e4m3_to_double(w[n * K + k]);
+      const double sw = (double)w_scale[w_scale_rows == 1 ? 0 : n];
+      store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc * sx * sw);
+    }
+  }
+  return ORC_OK;
+}

@@ -115,6 +115,15 @@ int orc_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N
                        const uint16_t* x, const uint16_t* w, int64_t n_rows, const int64_t* rows,
                        void* const* dst);
 
+/* FP8 producer: x [tp*S][K], w [N][K] e4m3 codes; x_scale 1 or tp*S fp32,
+ * w_scale 1 or N fp32; P = (x w^T) * x_scale[m] * w_scale[n], scattered as
+ * orc_matmul_scatter. */
+int orc_scaled_matmul_scatter(int32_t tp, int32_t rank, int64_t S, int64_t K, int64_t N,
+                              int32_t out_dtype, const uint8_t* x, const float* x_scale,
+                              int64_t x_scale_rows, const uint8_t* w, const float* w_scale,
+                              int64_t w_scale_rows, int64_t n_rows, const int64_t* rows,
+                              void* const* dst);
+
 /* Format helpers, exported so that the tests can pin them directly. */
 uint16_t orc_bf16_from_double(double x);   /* round to nearest, ties to even */
 double orc_bf16_to_double(uint16_t bits);

@@ -56,6 +56,10 @@ MUTATIONS = {
                               "    const int64_t s = m - r * S; /* its row in that rank's shard */",
                               "const int64_t r = m % tp;\n    const int64_t s = m / tp;"),
     "mm_weight_transposed": ("orc_bf16_to_double(w[n * K + k])", "orc_bf16_to_double(w[k * N + n])"),
+    "fp8_x_scale_dropped": ("store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc * sx * sw);",
+                            "store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc * sw);"),
+    "fp8_w_scale_by_token": ("const double sw = (double)w_scale[w_scale_rows == 1 ? 0 : n];",
+                             "const double sw = (double)w_scale[w_scale_rows == 1 ? 0 : m % N];"),
     "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
                              "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
     "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",

@@ -792,3 +792,62 @@ def test_producer_feeds_the_fused_path():
                                       None, 1e-6, oracle.QUANT_NONE, None, tp_rank=0, num_tokens=v)
         np.testing.assert_array_equal(a["out"], b["out"])
         np.testing.assert_array_equal(a["residual_out"], b["residual_out"])
+
+
+def _finite_e4m3_codes(rng, shape):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    return c
+
+
+def test_scaled_matmul_with_unit_scales_equals_bf16_matmul():
+    # every finite e4m3 value is exact in bf16, so the FP8 producer on codes
+    # equals the (pinned) bf16 producer on their bf16 images
+    rng = np.random.default_rng(8)
+    tp, S, K, N = 2, 3, 48, 5
+    x8 = _finite_e4m3_codes(rng, (tp * S, K))
+    w8 = _finite_e4m3_codes(rng, (N, K))
+    dec = np.vectorize(oracle.e4m3_to_double)
+    xb, wb = _bf16_bits(dec(x8).astype(np.float32)), _bf16_bits(dec(w8).astype(np.float32))
+    one = np.ones(1, np.float32)
+    for rank in range(tp):
+        a = oracle.scaled_matmul_scatter(x8, one, w8, one, tp=tp, rank=rank)
+        b = oracle.matmul_scatter(xb, wb, tp=tp, rank=rank)
+        for r in range(tp):
+            np.testing.assert_array_equal(a[r], b[r])
+
+
+def test_scaled_matmul_brute_force_with_row_and_column_scales():
+    rng = np.random.default_rng(9)
+    tp, S, K, N = 2, 2, 6, 3
+    x8 = _finite_e4m3_codes(rng, (tp * S, K))
+    w8 = _finite_e4m3_codes(rng, (N, K))
+    xs = rng.uniform(0.5, 2, tp * S).astype(np.float32)
+    ws = rng.uniform(0.5, 2, N).astype(np.float32)
+    dst = oracle.scaled_matmul_scatter(x8, xs, w8, ws, tp=tp, rank=1, out_dtype=oracle.ORC_F32)
+    for m in range(tp * S):
+        r, s = divmod(m, S)
+        for n in range(N):
+            dot = 0.0
+            for k in range(K):
+                dot += oracle.e4m3_to_double(int(x8[m, k])) * oracle.e4m3_to_double(int(w8[n, k]))
+            want = np.float32(dot * float(xs[m]) * float(ws[n]))
+            assert dst[r][1][s][n] == want, (m, n)
+
+
+def test_scaled_matmul_scale_placement():
+    # codes of 1.0 everywhere: P[m][n] = K * x_scale[m] * w_scale[n]; powers of
+    # two keep it exact and tell rows from columns
+    tp, S, K, N = 2, 4, 16, 6
+    x8 = np.full((tp * S, K), 0x38, np.uint8)
+    w8 = np.full((N, K), 0x38, np.uint8)
+    xs = (2.0 ** (np.arange(tp * S) % 4)).astype(np.float32)
+    ws = (2.0 ** -(np.arange(N) % 3)).astype(np.float32)
+    for xsc, wsc in ((xs, ws), (xs[:1], ws), (xs, ws[:1]), (xs[:1], ws[:1])):
+        dst = oracle.scaled_matmul_scatter(x8, xsc, w8, wsc, tp=tp, rank=0)
+        for m in range(tp * S):
+            r, s = divmod(m, S)
+            want = K * (xsc[0] if xsc.size == 1 else xs[m]) * (wsc if wsc.size > 1 else np.full(N, wsc[0]))
+            np.testing.assert_array_equal(dst[r][0][s], want.astype(np.float32))
+    with pytest.raises(oracle.OracleError):
+        oracle.scaled_matmul_scatter(x8, xs[:3], w8, ws, tp=tp, rank=0)   # neither 1 nor M scales
