@@ -53,8 +53,15 @@ MUTATIONS = {
     "mm_slot_of_destination": ("store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc);",
                                "store(dst[r], out_dtype, ((int64_t)r * S + s) * N + n, acc);"),
     "mm_round_robin_tokens": ("const int64_t r = m / S;     /* destination rank of this token */\n"
-                              "    const int64_t s = m - r * S; /* its row in that rank's shard */",
-                              "const int64_t r = m % tp;\n    const int64_t s = m / tp;"),
+                              "    const int64_t s = m - r * S; /* its row in that rank's shard */\n"
+                              "    for (int64_t n = 0; n < N; ++n) {",
+                              "const int64_t r = m % tp;\n    const int64_t s = m / tp;\n"
+                              "    for (int64_t n = 0; n < N; ++n) {"),
+    "fp8_round_robin_tokens": ("const int64_t r = m / S;     /* destination rank of this token */\n"
+                               "    const int64_t s = m - r * S; /* its row in that rank's shard */\n"
+                               "    const double sx",
+                               "const int64_t r = m % tp;\n    const int64_t s = m / tp;\n"
+                               "    const double sx"),
     "mm_weight_transposed": ("orc_bf16_to_double(w[n * K + k])", "orc_bf16_to_double(w[k * N + n])"),
     "fp8_x_scale_dropped": ("store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc * sx * sw);",
                             "store(dst[r], out_dtype, ((int64_t)rank * S + s) * N + n, acc * sw);"),
