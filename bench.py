@@ -186,6 +186,55 @@ def setup_gemm(w, dev):
     return (x, wt, dsts), launch, 2 * M * K * H, M, desc
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak, AMD published
+
+
+def setup_gemm_fp8(w, dev):
+    """The FP8 producer at the workload's shape: e4m3 codes x [T_pad, H/tp]
+    with per-token scales, weight [H, H/tp] with per-column scales, bf16
+    partials into the tp receive buffers."""
+    tp, S, H = w.tp, w.shard_rows, w.hidden
+    M, K = tp * S, H // tp
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed_index + 4)
+    x8 = torch.randint(0, 256, (M, K), generator=g, device=dev, dtype=torch.uint8)
+    w8 = torch.randint(0, 256, (H, K), generator=g, device=dev, dtype=torch.uint8)
+    x8[(x8 & 0x7F) == 0x7F] = 0x38   # no NaN codes
+    w8[(w8 & 0x7F) == 0x7F] = 0x38
+    xs = torch.rand((M,), generator=g, device=dev) * 0.01 + 0.001
+    ws = torch.rand((H,), generator=g, device=dev) * 0.01 + 0.001
+    dsts = [torch.empty((tp, S, H), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+
+    def launch():
+        sp.sp_scaled_matmul_scatter(x8, xs, w8, ws, dsts, rank=w.rank)
+
+    desc = (f"FP8 producer GEMM of rank {w.rank} of tp={tp}: e4m3 [{M}, {K}] x [{H}, {K}]^T, "
+            f"per-token and per-column fp32 scales, bf16 partials scattered to {tp} receive buffers")
+    return (x8, xs, w8, ws, dsts), launch, 2 * M * K * H, M, desc
+
+
+def library_fp8_gemm_us(x8, xs, w8, ws, steps=20):
+    """hipBLASLt through torch._scaled_mm on the same codes and scales, for
+    context only; None where this torch build does not offer it."""
+    try:
+        a = x8.view(torch.float8_e4m3fn)
+        b = w8.view(torch.float8_e4m3fn).t()
+        call = lambda: torch._scaled_mm(a, b, scale_a=xs.view(-1, 1), scale_b=ws.view(1, -1),
+                                        out_dtype=torch.bfloat16)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+    except Exception as e:  # noqa: BLE001 -- context only
+        return {"error": type(e).__name__ + ": " + str(e)[:120]}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1000 / steps, 2)
+
+
 def library_gemm_us(x, wt, steps=20):
     """hipBLASLt (torch's linear) on the same operands, for context only."""
     import torch.nn.functional as F
@@ -288,9 +337,10 @@ def main():
                          "the DSA-CP head-to-token exchange at the workload's tp, tokens and H; "
                          "gemm: one rank's producer GEMM (o_proj split along K) with its "
                          "ReduceScatter destinations")
-    ap.add_argument("--quant", default=None, choices=["mxfp8", "mxfp4"],
-                    help="replace the workload's output quantisation by block scaling "
-                         "(32-element E8M0 scales) with e4m3 or e2m1 elements")
+    ap.add_argument("--quant", default=None, choices=["mxfp8", "mxfp4", "fp8"],
+                    help="fused path: replace the workload's output quantisation by block "
+                         "scaling (32-element E8M0 scales) with e4m3 or e2m1 elements; gemm "
+                         "path: fp8 times the e4m3 producer (sp_scaled_matmul_scatter)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling hardware byte counters)")
@@ -300,13 +350,19 @@ def main():
               "and no collective is part of this build; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.quant == "fp8" and args.path != "gemm":
+        ap.error("--quant fp8 goes with --path gemm")
+    if args.path == "gemm" and args.quant not in (None, "fp8"):
+        ap.error("--path gemm takes --quant fp8 or nothing")
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(args, dev)
         return
     w = WORKLOADS[args.workload]
-    if args.quant:
+    fp8_gemm = args.path == "gemm" and args.quant == "fp8"
+    if args.quant and not args.path == "gemm":
         w = dataclasses.replace(w, quant_mode=QUANT_MX_BLOCK, out_dtype=torch.uint8,
                                 fp4=args.quant == "mxfp4")
     sp.load()
@@ -322,8 +378,8 @@ def main():
         x, launch, nbytes, tokens, desc = setup_dsacp(w, dev)
         desc = f"{w.name} {desc}"
     elif args.path == "gemm":
-        x, launch, nbytes, tokens, desc = setup_gemm(w, dev)  # nbytes: flops here
-        desc = f"{w.name} {desc}"
+        x, launch, nbytes, tokens, desc = (setup_gemm_fp8 if fp8_gemm else setup_gemm)(w, dev)
+        desc = f"{w.name} {desc}"  # nbytes holds the flops here
     else:
         x, launch, _ = setup(w, dev)
         nbytes, tokens = w.algorithmic_bytes(), w.valid_rows()
@@ -363,7 +419,7 @@ def main():
     ms_per_step = wall * 1000.0 / args.steps
     gemm = args.path == "gemm"
     scale = 1e12 if gemm else 1e9   # TFLOP/s for the GEMM, GB/s for the rest
-    peak = MFMA_BF16_PEAK_TFLOPS if gemm else HBM_PEAK_GBS
+    peak = (MFMA_FP8_PEAK_TFLOPS if fp8_gemm else MFMA_BF16_PEAK_TFLOPS) if gemm else HBM_PEAK_GBS
     value = nbytes / (ms_per_step / 1000.0) / scale
     achieved = nbytes / (avg_ms / 1000.0) / scale
     traffic = measured_traffic(w.name if args.path == "fused" and not args.quant else
@@ -372,7 +428,8 @@ def main():
 
     result = {
         "metric": METRIC if args.path == "fused" else
-        "achieved bf16 TFLOP/s (% of MI355X dense MFMA peak) for the producer GEMM" if gemm else
+        (f"achieved {'fp8' if fp8_gemm else 'bf16'} TFLOP/s (% of MI355X dense MFMA peak) for the "
+         "producer GEMM") if gemm else
         f"achieved HBM GB/s (% of MI355X peak) for {args.path} (one rank's share)",
         "value": round(value, 2),
         "unit": "TFLOP/s" if gemm else "GB/s",
@@ -384,14 +441,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         # the fused path computes in fp32; the layout paths move elements unchanged
-        "dtype": ("f32" if args.path == "fused" else "bf16" if args.path in ("fc2", "dsacp", "gemm")
+        "dtype": ("f32" if args.path == "fused" else "e4m3" if fp8_gemm else
+                  "bf16" if args.path in ("fc2", "dsacp", "gemm")
                   else {torch.uint8: "u8", torch.bfloat16: "bf16"}.get(w.out_dtype, "f32")),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.description}" if args.path == "fused" else desc,
             "path": {"fused": "sp_reduce_add_rmsnorm", "gather": "sp_all_gather_unpad",
                      "fc2": "sp_fc2_regroup", "dsacp": "sp_dsacp_heads_to_tokens",
-                     "gemm": "sp_matmul_scatter"}[args.path],
+                     "gemm": "sp_scaled_matmul_scatter" if fp8_gemm else "sp_matmul_scatter"}[args.path],
             "tp": w.tp, "rank": w.rank, "num_tokens": w.num_tokens,
             "shard_rows": w.shard_rows, "hidden": w.hidden,
             "quant": QUANT_NAMES[w.quant_mode] + (
@@ -399,8 +457,9 @@ def main():
             "deepstack": w.deepstack, "bias": w.bias,
             ("algorithmic_flops" if gemm else "algorithmic_bytes"): nbytes,
             # the GEMM moves x, w and its output once each
-            **({"algorithmic_bytes": 2 * (w.num_tokens_pad * (w.hidden // w.tp)
-                                          + w.hidden * (w.hidden // w.tp) + w.num_tokens_pad * w.hidden)}
+            **({"algorithmic_bytes": (1 if fp8_gemm else 2) * (w.num_tokens_pad * (w.hidden // w.tp)
+                                                                + w.hidden * (w.hidden // w.tp))
+                                     + 2 * w.num_tokens_pad * w.hidden}
                if gemm else {}),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -423,7 +482,11 @@ def main():
     }
     if args.cpu_budget > 0 and args.path == "fused":
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
-    if gemm:
+    if gemm and fp8_gemm:
+        result["context"] = {"hipblaslt_scaled_mm_us": library_fp8_gemm_us(x[0], x[1], x[2], x[3]),
+                             "note": "torch._scaled_mm (hipBLASLt) on the same codes and scales, "
+                                     "one [M, H] bf16 output, no scatter"}
+    elif gemm:
         result["context"] = {"hipblaslt_linear_us": round(library_gemm_us(x[0], x[1]), 2),
                              "note": "torch's linear (hipBLASLt) on the same operands, "
                                      "one [M, H] output, no scatter"}

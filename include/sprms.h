@@ -268,8 +268,11 @@ typedef struct {
   int64_t shard_rows;  /* S; x has M = tp*S token rows (padded), 0 <= M < 2^31 */
   int64_t k;           /* K, this rank's slice of the input features, K % 8 == 0, 8 <= K <= 2^20 */
   int64_t n;           /* N, output columns (the hidden size H), N % 8 == 0, 8 <= N <= 2^20 */
-  int32_t in_dtype;    /* SP_BF16 (x and w) */
+  int32_t in_dtype;    /* x and w: SP_BF16 (sp_matmul_scatter) or SP_FP8_E4M3
+                          (sp_scaled_matmul_scatter, then K % 16 == 0, 16 <= K) */
   int32_t out_dtype;   /* SP_BF16 | SP_F32: the partial dtype of the fused call */
+  int64_t x_scale_rows;  /* e4m3 only: 1 (per-tensor scale) or M (per-token); 0 for bf16 */
+  int64_t w_scale_rows;  /* e4m3 only: 1 (per-tensor scale) or N (per output column); 0 for bf16 */
 } sp_matmul_problem;
 
 /*
@@ -298,11 +301,28 @@ typedef struct {
  *        On one GPU these are local; on a node, peer-mapped buffers.
  *
  * Pointers 16-byte aligned; the written slots must not overlap x, w or each
- * other.  M == 0 enqueues nothing.  Same error convention as
- * sp_reduce_add_rmsnorm.
+ * other.  x_scale_rows and w_scale_rows must be 0.  M == 0 enqueues nothing.
+ * Same error convention as sp_reduce_add_rmsnorm.
  */
 int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, void* const* dst,
                       void* stream);
+
+/*
+ * sp_scaled_matmul_scatter -- the FP8 form of the producer (vLLM SP /
+ * AsyncTP / quantisation notes, §4: after sequence parallelism the
+ * row-parallel GEMM is an FP8 GEMM with its scales, fused with the
+ * ReduceScatter): x and w hold OCP e4m3 codes and
+ *
+ *   P[m][n] = (sum over k of x[m][k] * w[n][k]) * x_scale[m or 0] * w_scale[n or 0]
+ *
+ * (products exact, fp32 accumulation on the matrix cores, the two scales
+ * applied to the fp32 sum), scattered and rounded exactly as
+ * sp_matmul_scatter.  x_scale: device fp32 [x_scale_rows], w_scale: device
+ * fp32 [w_scale_rows], 4-byte aligned.  Other arguments and errors as for
+ * sp_matmul_scatter; p->in_dtype must be SP_FP8_E4M3.
+ */
+int sp_scaled_matmul_scatter(const sp_matmul_problem* p, const void* x, const float* x_scale,
+                             const void* w, const float* w_scale, void* const* dst, void* stream);
 
 /*
  * sp_validate -- the host-side checks of sp_reduce_add_rmsnorm, alone.

@@ -30,7 +30,8 @@ SP_OK, SP_ERR_NULL, SP_ERR_SHAPE, SP_ERR_DTYPE, SP_ERR_ALIGN, SP_ERR_UNSUPPORTED
     0, -1, -2, -3, -4, -5, -6)
 
 EXPORTED = ("sp_reduce_add_rmsnorm", "sp_validate", "sp_all_gather_unpad", "sp_fc2_regroup",
-            "sp_dsacp_heads_to_tokens", "sp_matmul_scatter", "sp_shard_geometry",
+            "sp_dsacp_heads_to_tokens", "sp_matmul_scatter", "sp_scaled_matmul_scatter",
+            "sp_shard_geometry",
             "sp_error_string", "sp_last_error")
 SP_FLAG_VALID_ROWS_ONLY = 1
 
@@ -102,6 +103,8 @@ class sp_matmul_problem(C.Structure):
         ("n", C.c_int64),
         ("in_dtype", C.c_int32),
         ("out_dtype", C.c_int32),
+        ("x_scale_rows", C.c_int64),
+        ("w_scale_rows", C.c_int64),
     ]
 
 
@@ -136,6 +139,9 @@ def load(build_if_missing: bool = False):
     lib.sp_dsacp_heads_to_tokens.restype = C.c_int
     lib.sp_matmul_scatter.argtypes = [C.POINTER(sp_matmul_problem), vp, vp, C.POINTER(vp), vp]
     lib.sp_matmul_scatter.restype = C.c_int
+    lib.sp_scaled_matmul_scatter.argtypes = [C.POINTER(sp_matmul_problem), vp, vp, vp, vp,
+                                             C.POINTER(vp), vp]
+    lib.sp_scaled_matmul_scatter.restype = C.c_int
     lib.sp_shard_geometry.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64),
                                       C.POINTER(i64)]
     lib.sp_shard_geometry.restype = C.c_int
@@ -390,6 +396,35 @@ def sp_matmul_scatter(x, w, dsts, *, rank: int, stream=None) -> None:
     with torch.cuda.device(x.device):
         _check(lib.sp_matmul_scatter(C.byref(p), _addr(x), _addr(w), dst,
                                      _stream_handle(x.device, stream)))
+
+
+def sp_scaled_matmul_scatter(x, x_scale, w, w_scale, dsts, *, rank: int, stream=None) -> None:
+    """FP8 producer: x [tp*S, K] and w [N, K] e4m3 codes (uint8 or
+    float8_e4m3fn), x_scale [1] or [tp*S] and w_scale [1] or [N] float32;
+    (x w^T) x_scale w_scale written into slot `rank` of each dsts[r]
+    [tp, S, N] (bf16 or f32).  See include/sprms.h."""
+    lib = load()
+    tp = len(dsts)
+    M, K = x.shape
+    N = w.shape[0]
+    if M % tp or w.shape[1] != K:
+        raise ValueError("x must be [tp*S, K] and w [N, K]")
+    S = M // tp
+    for d in dsts:
+        if d.shape != (tp, S, N) or d.dtype != dsts[0].dtype:
+            raise ValueError("every receive buffer must be [tp, S, N] of one dtype")
+    if x_scale.dtype != torch.float32 or w_scale.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    _same_device(x, x_scale, w, w_scale, dsts)
+    p = sp_matmul_problem(tp=tp, rank=rank, shard_rows=S, k=K, n=N, in_dtype=_sp_dtype(x.dtype),
+                          out_dtype=_sp_dtype(dsts[0].dtype), x_scale_rows=x_scale.numel(),
+                          w_scale_rows=w_scale.numel())
+    if _sp_dtype(w.dtype) != p.in_dtype:
+        raise ValueError("x and w must share a dtype")
+    dst = (C.c_void_p * tp)(*[_addr(d) for d in dsts])
+    with torch.cuda.device(x.device):
+        _check(lib.sp_scaled_matmul_scatter(C.byref(p), _addr(x), _addr(x_scale), _addr(w),
+                                            _addr(w_scale), dst, _stream_handle(x.device, stream)))
 
 
 def sp_validate(problem: sp_problem, partials, residual, weight, bias, eps, quant_mode, deepstack,

@@ -64,18 +64,22 @@ constexpr int kGroupM = 4;               // token bands per tile group
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct MArgs {
-  const char* x;            // [M][K] bf16
-  const char* w;            // [N][K] bf16
+  const char* x;            // [M][K] bf16 or e4m3
+  const char* w;            // [N][K] bf16 or e4m3
+  const float* x_scale;     // e4m3 inputs: 1 or M entries (per tensor / per token)
+  const float* w_scale;     // e4m3 inputs: 1 or N entries (per tensor / per column)
   char* dst[kMaxTp];        // rank r's [tp][S][N] receive buffer
   int64_t S;
   int64_t slot;             // rank * S: first row of this rank's slot
   int32_t M, N, K;
   int32_t tiles_m, tiles_n;
+  int32_t x_scale_rows, w_scale_rows;
 };
 
 // tile id of workgroup b: XCD-contiguous ranges over a grouped order
@@ -97,8 +101,16 @@ __device__ __forceinline__ void tile_of(const MArgs& a, int* tm, int* tn) {
 // physical 16-byte chunk of logical chunk c in LDS row `row`
 __device__ __forceinline__ int swizzle(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int OUT>
+// IN: SP_BF16 (v_mfma_f32_32x32x16_bf16, K 16 a step) or SP_FP8_E4M3
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales, K 64 a step,
+// the input scales applied in the epilogue).  Either way an LDS row is 128
+// bytes per stage: 64 bf16 or 128 e4m3 elements of K.
+template <int OUT, int IN>
 __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a) {
+  constexpr bool fp8 = IN == SP_FP8_E4M3;
+  constexpr int E = fp8 ? 1 : 2;                 // input bytes per element
+  constexpr int BK = kBK * 2 / E;                // K elements per stage
+  constexpr int KSTEP = fp8 ? 64 : 16;           // K elements per MFMA
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   int tm, tn;
   tile_of(a, &tm, &tn);
@@ -108,7 +120,7 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   const int wm = wave >> 1, wn = wave & 1;  // tokens [wm*64, +64), columns [wn*128, +128)
 
   // per-tile descriptors: rows past M (N) read as zero
-  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * E;
   const int rows_x = a.M - m0 < kBM ? a.M - m0 : kBM;
   const int rows_w = a.N - n0 < kBN ? a.N - n0 : kBN;
   const rsrc_t gx = row_rsrc(a.x + static_cast<int64_t>(m0) * row_bytes, static_cast<uint32_t>(rows_x) * row_bytes);
@@ -123,9 +135,9 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
     for (int t = 0; t < kBM / 8 / (kThreads / 64); ++t) {
       const int g = wave + (kThreads / 64) * t;  // group of 8 rows
       const int row = g * 8 + grow;
-      const int k = kb + swizzle(row, pchunk) * 8;
+      const int k = kb + swizzle(row, pchunk) * (16 / E);  // first element of the chunk
       const uint32_t oob = (static_cast<uint32_t>(k - a.K) >> 31) ? 0u : 0x80000000u;
-      const uint32_t off = (static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(k) * 2u) | oob;
+      const uint32_t off = (static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(k) * E) | oob;
       char* base = smem + stage * kStageBytes + g * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(gw, (lds_void*)base, 16, off, 0, 0, kCachedPolicy);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(gx, (lds_void*)(base + kOpBytes), 16, off, 0, 0, kCachedPolicy);
@@ -140,37 +152,53 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = (a.K + kBK - 1) / kBK;
+  const int nk = (a.K + BK - 1) / BK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // operand rows of this lane: row l%32 of each 32-row block, K half l/32
+  // of each MFMA step (bf16: one 16-byte chunk; e4m3: two)
   const int arow = wn * 128 + (lane & 31), brow = wm * 64 + (lane & 31);
   const int khalf = lane >> 5;
+  constexpr int kChunks = KSTEP * E / 16 / 2;    // chunks per lane and step: 1 or 2
+  auto frag = [&](const char* op, int r, int ks) {
+    const int c = ks * 2 * kChunks + khalf * kChunks;
+    if constexpr (fp8) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(op + r * 128 + swizzle(r, c) * 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(op + r * 128 + swizzle(r, c + 1) * 16);
+      const i32x8 v = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                       static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                       static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      return v;
+    } else {
+      return *reinterpret_cast<const bf16x8*>(op + r * 128 + swizzle(r, c) * 16);
+    }
+  };
+  using Frag = decltype(frag(smem, 0, 0));
   for (int kt = 0; kt < nk; ++kt) {
     // the next step's loads (past K on the last step: zeros into the idle stage)
-    issue((kt + 1) & 1, (kt + 1) * kBK);
+    issue((kt + 1) & 1, (kt + 1) * BK);
     const char* sw = smem + (kt & 1) * kStageBytes;
     const char* sx = sw + kOpBytes;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = ks * 2 + khalf;
-      bf16x8 fa[4], fb[2];
+    for (int ks = 0; ks < BK / KSTEP; ++ks) {
+      Frag fa[4], fb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = arow + i * 32;
-        fa[i] = *reinterpret_cast<const bf16x8*>(sw + r * 128 + swizzle(r, c) * 16);
-      }
+      for (int i = 0; i < 4; ++i) fa[i] = frag(sw, arow + i * 32, ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = brow + j * 32;
-        fb[j] = *reinterpret_cast<const bf16x8*>(sx + r * 128 + swizzle(r, c) * 16);
-      }
+      for (int j = 0; j < 2; ++j) fb[j] = frag(sx, brow + j * 32, ks);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (fp8) {
+            // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 code 127)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
+                                                                         127, 0, 127);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the next stage have landed
     __syncthreads();
@@ -191,13 +219,27 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
     for (int j = 0; j < 2; ++j) {
       const int ml = wm * 64 + j * 32 + (lane & 31) - pass * rows_per_pass;
       if (ml < 0 || ml >= rows_per_pass) continue;
+      float sx = 1.0f;
+      if constexpr (fp8) {  // token scale; rows past M (not stored) read entry 0
+        const int m = m0 + pass * rows_per_pass + ml;
+        sx = a.x_scale[a.x_scale_rows == 1 || m >= a.M ? 0 : m];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int nl = wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-          const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-          const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+          float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          if constexpr (fp8) {  // column scales; columns past N (not stored) read entry 0
+            const int n = n0 + nl;
+            const bool per_col = a.w_scale_rows != 1 && n < a.N;
+            const float* sw = a.w_scale + (per_col ? n : 0);
+            v0 = v0 * sx * sw[0];
+            v1 = v1 * sx * sw[per_col ? 1 : 0];
+            v2 = v2 * sx * sw[per_col ? 2 : 0];
+            v3 = v3 * sx * sw[per_col ? 3 : 0];
+          }
           char* dst = smem + ml * out_row + nl * esz;
           if constexpr (OUT == SP_F32) {
             const f32x4 v = {v0, v1, v2, v3};
@@ -225,42 +267,56 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   }
 }
 
-}  // namespace
-
-extern "C" {
-
-int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, void* const* dst,
-                      void* stream) {
-  if (!p) return fail(SP_ERR_NULL, "matmul descriptor is NULL");
+// Validation and launch shared by both entry points; x_scale / w_scale are
+// NULL for bf16 inputs.
+int launch_matmul(const sp_matmul_problem* p, const void* x, const float* x_scale, const void* w,
+                  const float* w_scale, void* const* dst, void* stream) {
+  const bool fp8 = p->in_dtype == SP_FP8_E4M3;
   const int tp = p->tp;
   if (tp < 1 || tp > kMaxTp) return fail(SP_ERR_SHAPE, "tp=%d outside [1, %d]", tp, kMaxTp);
   if (p->rank < 0 || p->rank >= tp) return fail(SP_ERR_SHAPE, "rank=%d outside [0, %d)", p->rank, tp);
-  if (p->in_dtype != SP_BF16) return fail(SP_ERR_DTYPE, "in_dtype=%d: only SP_BF16 inputs", p->in_dtype);
   if (p->out_dtype != SP_BF16 && p->out_dtype != SP_F32)
     return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_BF16 or SP_F32", p->out_dtype);
   const int64_t S = p->shard_rows, K = p->k, N = p->n;
   const int64_t M = S * tp;
   if (S < 0 || M > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
-  if (K < 8 || K % 8 != 0 || K > (1 << 20))
-    return fail(SP_ERR_SHAPE, "k=%lld must be a multiple of 8 in [8, 2^20]", (long long)K);
+  const int64_t kq = fp8 ? 16 : 8;  // K elements per 16-byte chunk
+  if (K < kq || K % kq != 0 || K > (1 << 20))
+    return fail(SP_ERR_SHAPE, "k=%lld must be a multiple of %lld in [%lld, 2^20]", (long long)K, (long long)kq,
+                (long long)kq);
   if (N < 8 || N % 8 != 0 || N > (1 << 20))
     return fail(SP_ERR_SHAPE, "n=%lld must be a multiple of 8 in [8, 2^20]", (long long)N);
+  if (fp8) {
+    if (p->x_scale_rows != 1 && p->x_scale_rows != M)
+      return fail(SP_ERR_SHAPE, "x_scale_rows=%lld must be 1 or M=%lld", (long long)p->x_scale_rows, (long long)M);
+    if (p->w_scale_rows != 1 && p->w_scale_rows != N)
+      return fail(SP_ERR_SHAPE, "w_scale_rows=%lld must be 1 or N=%lld", (long long)p->w_scale_rows, (long long)N);
+  } else if (p->x_scale_rows != 0 || p->w_scale_rows != 0) {
+    return fail(SP_ERR_SHAPE, "bf16 inputs take no scales (x_scale_rows and w_scale_rows must be 0)");
+  }
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   if (tiles > INT32_MAX) return fail(SP_ERR_SHAPE, "too many tiles for one grid");
   if (M == 0) return SP_OK;
   if (!x || !w || !dst) return fail(SP_ERR_NULL, "x, w and dst must be non-NULL");
+  if (fp8 && (!x_scale || !w_scale)) return fail(SP_ERR_NULL, "x_scale and w_scale must be non-NULL");
   if (misaligned(x) || misaligned(w)) return fail(SP_ERR_ALIGN, "x and w must be 16-byte aligned");
+  if (fp8 && (misaligned(x_scale, 4) || misaligned(w_scale, 4)))
+    return fail(SP_ERR_ALIGN, "x_scale and w_scale must be 4-byte aligned");
   const size_t e = p->out_dtype == SP_F32 ? 4 : 2;
   const size_t slot_n = static_cast<size_t>(S) * N * e;  // bytes this rank writes per destination
-  const size_t x_n = static_cast<size_t>(M) * K * 2, w_n = static_cast<size_t>(N) * K * 2;
+  const size_t ie = fp8 ? 1 : 2;
+  const size_t x_n = static_cast<size_t>(M) * K * ie, w_n = static_cast<size_t>(N) * K * ie;
+  const size_t xs_n = fp8 ? static_cast<size_t>(p->x_scale_rows) * 4 : 0;
+  const size_t ws_n = fp8 ? static_cast<size_t>(p->w_scale_rows) * 4 : 0;
   MArgs ma;
   memset(&ma, 0, sizeof ma);
   for (int r = 0; r < tp; ++r) {
     if (!dst[r]) return fail(SP_ERR_NULL, "dst[%d] is NULL", r);
     if (misaligned(dst[r])) return fail(SP_ERR_ALIGN, "dst[%d] is not 16-byte aligned", r);
     const char* slot = static_cast<const char*>(dst[r]) + static_cast<size_t>(p->rank) * slot_n;
-    if (overlap(slot, slot_n, x, x_n) || overlap(slot, slot_n, w, w_n))
-      return fail(SP_ERR_SHAPE, "dst[%d] slot %d overlaps x or w", r, p->rank);
+    if (overlap(slot, slot_n, x, x_n) || overlap(slot, slot_n, w, w_n) ||
+        overlap(slot, slot_n, x_scale, xs_n) || overlap(slot, slot_n, w_scale, ws_n))
+      return fail(SP_ERR_SHAPE, "dst[%d] slot %d overlaps an input", r, p->rank);
     for (int r2 = 0; r2 < r; ++r2) {
       const char* other = static_cast<const char*>(dst[r2]) + static_cast<size_t>(p->rank) * slot_n;
       if (overlap(slot, slot_n, other, slot_n))
@@ -270,6 +326,10 @@ int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, 
   }
   ma.x = static_cast<const char*>(x);
   ma.w = static_cast<const char*>(w);
+  ma.x_scale = x_scale;
+  ma.w_scale = w_scale;
+  ma.x_scale_rows = static_cast<int32_t>(p->x_scale_rows);
+  ma.w_scale_rows = static_cast<int32_t>(p->w_scale_rows);
   ma.S = S;
   ma.slot = static_cast<int64_t>(p->rank) * S;
   ma.M = static_cast<int32_t>(M);
@@ -278,12 +338,34 @@ int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, 
   ma.tiles_m = static_cast<int32_t>((M + kBM - 1) / kBM);
   ma.tiles_n = static_cast<int32_t>((N + kBN - 1) / kBN);
   void* args[] = {&ma};
-  const void* fn = p->out_dtype == SP_F32 ? reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_F32>)
-                                          : reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_BF16>);
+  const bool f32 = p->out_dtype == SP_F32;
+  const void* fn = fp8 ? (f32 ? reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_F32, SP_FP8_E4M3>)
+                              : reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_BF16, SP_FP8_E4M3>))
+                       : (f32 ? reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_F32, SP_BF16>)
+                              : reinterpret_cast<const void*>(&matmul_scatter_kernel<SP_BF16, SP_BF16>));
   hipError_t err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(SP_ERR_HIP, "matmul launch failed: %s", hipGetErrorString(err));
   return SP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp_matmul_scatter(const sp_matmul_problem* p, const void* x, const void* w, void* const* dst,
+                      void* stream) {
+  if (!p) return fail(SP_ERR_NULL, "matmul descriptor is NULL");
+  if (p->in_dtype != SP_BF16) return fail(SP_ERR_DTYPE, "in_dtype=%d: sp_matmul_scatter takes SP_BF16", p->in_dtype);
+  return launch_matmul(p, x, nullptr, w, nullptr, dst, stream);
+}
+
+int sp_scaled_matmul_scatter(const sp_matmul_problem* p, const void* x, const float* x_scale,
+                             const void* w, const float* w_scale, void* const* dst, void* stream) {
+  if (!p) return fail(SP_ERR_NULL, "matmul descriptor is NULL");
+  if (p->in_dtype != SP_FP8_E4M3)
+    return fail(SP_ERR_DTYPE, "in_dtype=%d: sp_scaled_matmul_scatter takes SP_FP8_E4M3", p->in_dtype);
+  return launch_matmul(p, x, x_scale, w, w_scale, dst, stream);
 }
 
 }  // extern "C"

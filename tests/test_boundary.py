@@ -295,14 +295,46 @@ def test_fc2_regroup_empty_is_a_no_op():
 
 
 def _mm(tp=4, rank=1, S=64, K=896, N=1024, in_dtype=sp.SP_BF16, out_dtype=sp.SP_F32, x=BASE,
-        w=BASE + GB, dst=None):
+        w=BASE + GB, dst=None, xs_rows=0, ws_rows=0, scaled=False, xs=BASE + 60 * GB,
+        ws=BASE + 61 * GB):
     import ctypes as C
     lib = sp.load()
     p = sp.sp_matmul_problem(tp=tp, rank=rank, shard_rows=S, k=K, n=N, in_dtype=in_dtype,
-                             out_dtype=out_dtype)
+                             out_dtype=out_dtype, x_scale_rows=xs_rows, w_scale_rows=ws_rows)
     dst = dst if dst is not None else [BASE + (2 + r) * GB for r in range(max(tp, 1))]
     d = (C.c_void_p * len(dst))(*dst)
-    return lib.sp_matmul_scatter(C.byref(p), x, w, d, None), sp.sp_last_error()
+    if scaled:
+        rc = lib.sp_scaled_matmul_scatter(C.byref(p), x, xs, w, ws, d, None)
+    else:
+        rc = lib.sp_matmul_scatter(C.byref(p), x, w, d, None)
+    return rc, sp.sp_last_error()
+
+
+FP8 = dict(scaled=True, in_dtype=sp.SP_FP8_E4M3, xs_rows=1, ws_rows=1)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(FP8, in_dtype=sp.SP_BF16), sp.SP_ERR_DTYPE),
+    (dict(FP8, K=24), sp.SP_ERR_SHAPE),                  # e4m3 chunks are 16 elements
+    (dict(FP8, K=8), sp.SP_ERR_SHAPE),
+    (dict(FP8, xs_rows=3), sp.SP_ERR_SHAPE),             # neither 1 nor M = 256
+    (dict(FP8, xs_rows=0), sp.SP_ERR_SHAPE),
+    (dict(FP8, ws_rows=1023), sp.SP_ERR_SHAPE),          # neither 1 nor N = 1024
+    (dict(FP8, xs=0), sp.SP_ERR_NULL),
+    (dict(FP8, ws=0), sp.SP_ERR_NULL),
+    (dict(FP8, xs=BASE + 60 * GB + 2), sp.SP_ERR_ALIGN),
+    # slot 1 of dst[2] starts at BASE + 4 GB + 64*1024*4: a per-token scale there overlaps it
+    (dict(FP8, xs_rows=256, xs=BASE + 4 * GB + 64 * 1024 * 4), sp.SP_ERR_SHAPE),
+    (dict(xs_rows=1), sp.SP_ERR_SHAPE),                   # the bf16 entry takes no scales
+    (dict(in_dtype=sp.SP_FP8_E4M3), sp.SP_ERR_DTYPE),     # e4m3 goes through the scaled entry
+])
+def test_scaled_matmul_scatter_rejects_invalid_problems(case, expect):
+    status, msg = _mm(**case)
+    assert status == expect, msg
+
+
+def test_scaled_matmul_scatter_empty_is_a_no_op():
+    assert _mm(S=0, x=0, w=0, **FP8)[0] == sp.SP_OK
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -355,6 +387,8 @@ def test_binding_refuses_host_tensors():
         sp.sp_fc2_regroup([x[0], x[1]], [x[0].clone(), x[1].clone()], otp=1)
     with pytest.raises(ValueError):
         sp.sp_dsacp_heads_to_tokens([x[0], x[1]], [x[0].clone(), x[1].clone()])
+    with pytest.raises(ValueError):
+        sp.sp_matmul_scatter(x[0], x[1], [x.clone()], rank=0)
 
 
 def test_plain_c_client_compiles_links_and_runs(tmp_path):

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import reduce_add_rmsnorm_amd as sp
-from helpers import bf16_bits_to_f64, bf16_round, to_host, within_rounding
+from helpers import bf16_bits_to_f64, bf16_round, e4m3_decode, to_host, within_rounding
 from parity import run_case
 from reduce_add_rmsnorm_amd.inputs import QUANT_DYNAMIC_TOKEN, QUANT_NONE, WORKLOADS
 
@@ -208,3 +208,109 @@ def test_matmul_scatter_rejects_bad_calls(dev):
     assert e.value.status == sp.SP_ERR_SHAPE
     with pytest.raises(ValueError):
         sp.sp_matmul_scatter(x, w.cpu(), dsts, rank=0)
+
+
+# ------------------------------------------------------------- FP8 producer
+
+
+def _e4m3_codes(shape, dev, g):
+    c = torch.randint(0, 256, shape, generator=g, device=dev, dtype=torch.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38       # no NaN codes
+    return c
+
+
+def _check_fp8(x8, xs, w8, ws, dsts, rank, rows=None):
+    tp = len(dsts)
+    M, K = x8.shape
+    N = w8.shape[0]
+    S = M // tp
+    f32 = dsts[0].dtype == torch.float32
+    rows = np.arange(M) if rows is None else np.asarray(sorted(set(int(m) for m in rows)))
+    hx, hw = x8.cpu().numpy(), w8.cpu().numpy()
+    hxs, hws = xs.cpu().numpy(), ws.cpu().numpy()
+    ref32 = oracle.scaled_matmul_scatter(hx, hxs, hw, hws, tp=tp, rank=rank, out_dtype=oracle.ORC_F32,
+                                         rows=rows)
+    ax = np.abs(e4m3_decode(hx[rows])).astype(np.float32)   # e4m3 products are exact in fp32
+    aw = np.abs(e4m3_decode(hw)).astype(np.float32)
+    A = ax.astype(np.float64) @ aw.T.astype(np.float64)      # sum_k |x_k w_k|, for the bound only
+    sw = np.abs(hws.astype(np.float64)) if hws.size > 1 else np.full(N, abs(float(hws[0])))
+    steps = -(-K // 64)
+    for i, m in enumerate(rows):
+        r, s = divmod(int(m), S)
+        sx = abs(float(hxs[m if hxs.size > 1 else 0]))
+        want = ref32[r][rank][s].astype(np.float64)
+        pmax = (ax[i][None, :] * aw).max(axis=1).astype(np.float64)   # max_k |x_k w_k|
+        # the e4m3 MFMA sums each step of 64 products (zero-padded past K)
+        # with the small ones cut below 2^-11 of the largest -- measured on
+        # the device at 2^-11.6 -- and the steps are added in fp32
+        E = (steps * 2.0 ** -11 * pmax + (steps + 2) * 2.0 ** -24 * A[i]) * sx * sw + 3 * 2.0 ** -24 * np.abs(want)
+        got_t = dsts[r][rank, s]
+        if f32:
+            got = got_t.cpu().numpy().astype(np.float64)
+            assert (np.abs(got - want) <= E).all(), f"row {m}: f32 partial outside the bound"
+        else:
+            bits = to_host(got_t)
+            ok = within_rounding(bf16_bits_to_f64(bits), want - E, want + E, bf16_round)
+            assert ok.all(), f"row {m}: bf16 partial outside the bound at {np.argwhere(~ok)[:4].tolist()}"
+
+
+@pytest.mark.parametrize("tp,S,K,N,dtype,per_token,per_col", [
+    (2, 300, 144, 520, torch.float32, True, True),    # ragged M, N, a K tail of 16
+    (2, 300, 144, 520, torch.bfloat16, False, True),
+    (4, 64, 128, 256, torch.bfloat16, True, False),   # one tile, one K stage
+    (1, 5, 16, 8, torch.float32, False, False),       # smallest
+    (8, 33, 896, 1024, torch.bfloat16, True, True),
+])
+def test_scaled_matmul_scatter_matches_oracle(dev, tp, S, K, N, dtype, per_token, per_col):
+    M = tp * S
+    say(f"scaled_matmul_scatter tp={tp} S={S} K={K} N={N} {dtype} token={per_token} col={per_col}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(M + K + N)
+    x8, w8 = _e4m3_codes((M, K), dev, g), _e4m3_codes((N, K), dev, g)
+    xs = torch.rand((M if per_token else 1,), generator=g, device=dev) * 0.02 + 0.001
+    ws = torch.rand((N if per_col else 1,), generator=g, device=dev) * 0.02 + 0.001
+    for rank in sorted({0, tp - 1}):
+        dsts = _receive_buffers(tp, S, N, dtype, dev)
+        sp.sp_scaled_matmul_scatter(x8, xs, w8, ws, dsts, rank=rank)
+        torch.cuda.synchronize()
+        _check_fp8(x8, xs, w8, ws, dsts, rank)
+        _slots_untouched(dsts, rank)
+
+
+def test_scaled_matmul_scatter_exact_on_integer_codes(dev):
+    # codes of small integers and power-of-two scales: every step exact
+    tp, S, K, N = 2, 96, 256, 384
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    table = torch.tensor([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0xC8], dtype=torch.uint8,
+                         device=dev)                 # 0, 1, 2, 3, 4, -1, -2, -3, -4
+    x8 = table[torch.randint(0, 9, (tp * S, K), generator=g, device=dev)]
+    w8 = table[torch.randint(0, 9, (N, K), generator=g, device=dev)]
+    xs = 2.0 ** -torch.randint(0, 4, (tp * S,), generator=g, device=dev).float()
+    ws = 2.0 ** -torch.randint(0, 4, (N,), generator=g, device=dev).float()
+    dsts = _receive_buffers(tp, S, N, torch.float32, dev)
+    sp.sp_scaled_matmul_scatter(x8, xs, w8, ws, dsts, rank=1)
+    torch.cuda.synchronize()
+    ref = oracle.scaled_matmul_scatter(x8.cpu().numpy(), xs.cpu().numpy(), w8.cpu().numpy(),
+                                       ws.cpu().numpy(), tp=tp, rank=1)
+    for r in range(tp):
+        np.testing.assert_array_equal(dsts[r][1].cpu().numpy(), ref[r][1])
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_scaled_matmul_scatter_full_size_sampled_rows(dev, name):
+    w_ = WORKLOADS[name]
+    tp, S, H = w_.tp, w_.shard_rows, w_.hidden
+    M, K = tp * S, H // tp
+    say(f"scaled_matmul_scatter {name}: M={M} K={K} N={H} rank {w_.rank}, sampled rows")
+    g = torch.Generator(device=dev)
+    g.manual_seed(12)
+    x8, w8 = _e4m3_codes((M, K), dev, g), _e4m3_codes((H, K), dev, g)
+    xs = torch.rand((M,), generator=g, device=dev) * 0.01 + 0.001
+    ws = torch.rand((1,), generator=g, device=dev) * 0.01 + 0.001
+    dsts = [torch.empty((tp, S, H), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+    sp.sp_scaled_matmul_scatter(x8, xs, w8, ws, dsts, rank=w_.rank)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    rows = [0, 255, 256, S - 1, S, M - 1] + list(rng.integers(0, M, 16))
+    _check_fp8(x8, xs, w8, ws, dsts, w_.rank, rows=rows)
