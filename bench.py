@@ -354,6 +354,8 @@ def main():
         ap.error("--quant fp8 goes with --path gemm")
     if args.path == "gemm" and args.quant not in (None, "fp8"):
         ap.error("--path gemm takes --quant fp8 or nothing")
+    if args.path in ("gather", "fc2", "dsacp") and args.quant:
+        ap.error(f"--path {args.path} takes no --quant")
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -271,15 +271,17 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
 
 
 def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, *,
-            tp_rank: int, num_tokens: int, residual_out=None, out_dtype: Optional[int] = None,
-            stream=None):
+            tp_rank: int, num_tokens: int, residual_out=None, valid_rows_only: bool = False,
+            out_dtype: Optional[int] = None, partial_scale: float = 1.0, stream=None):
     """Marshal the arguments of sp_reduce_add_rmsnorm once and return a
     no-argument callable that enqueues the call again (for timing loops).
     The tensors must stay alive and in place while the callable is used."""
     lib = load()
     _same_device(partials, residual, weight, bias, deepstack, out, out_scale, residual_out)
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
-                        deepstack=deepstack, residual_out=residual_out, out_dtype=out_dtype)
+                        deepstack=deepstack, residual_out=residual_out,
+                        valid_rows_only=valid_rows_only, out_dtype=out_dtype,
+                        partial_scale=partial_scale)
     if stream is None:
         stream = torch.cuda.current_stream(partials.device)
     handle = stream if isinstance(stream, int) else stream.cuda_stream

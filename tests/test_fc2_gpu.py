@@ -178,3 +178,30 @@ def test_partial_scale_power_of_two_is_exact_scaling(dev):
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+
+
+def test_prepared_launch_equals_the_direct_call(dev):
+    # the marshalled launcher the benchmark times, with every option set
+    w = WORKLOADS["C2"]
+    x = make_inputs(w, rank=7, device=dev)
+    outs = []
+    for prepared in (False, True):
+        out = torch.full((w.shard_rows, w.hidden), 0x3F, dtype=torch.uint8, device=dev)
+        ro = torch.full((w.shard_rows, w.hidden), 2.0, dtype=torch.bfloat16, device=dev)
+        sc = torch.full((w.shard_rows,), -1.0, device=dev)
+        kw = dict(tp_rank=7, num_tokens=w.num_tokens, residual_out=ro, valid_rows_only=True,
+                  partial_scale=0.75)
+        args = (x["partials"], x["residual"], x["weight"], None, w.eps, QUANT_DYNAMIC_TOKEN, None, out, sc)
+        if prepared:
+            launch = sp.prepare(*args, **kw)
+            launch()
+            launch()   # repeat: same bytes
+        else:
+            sp.sp_reduce_add_rmsnorm(*args, **kw)
+        torch.cuda.synchronize()
+        outs.append((out, ro, sc))
+    (o1, r1, s1), (o2, r2, s2) = outs
+    assert torch.equal(o1, o2) and torch.equal(r1.view(torch.int16), r2.view(torch.int16))
+    assert torch.equal(s1, s2)
+    v = w.num_tokens - 7 * w.shard_rows
+    assert (o2[v:] == 0x3F).all() and (s2[v:] == -1.0).all()   # padding rows untouched
