@@ -314,3 +314,27 @@ def test_scaled_matmul_scatter_full_size_sampled_rows(dev, name):
     rng = np.random.default_rng(2)
     rows = [0, 255, 256, S - 1, S, M - 1] + list(rng.integers(0, M, 16))
     _check_fp8(x8, xs, w8, ws, dsts, w_.rank, rows=rows)
+
+
+@pytest.mark.parametrize("tp,S,K,N", [(64, 3, 64, 64), (3, 1, 16, 8)])
+def test_producers_at_group_and_size_extremes(dev, tp, S, K, N):
+    # 64 destinations inside one tile; a 3-token problem
+    M = tp * S
+    say(f"producers at extremes: tp={tp} S={S} K={K} N={N}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(tp + S)
+    x, w = _operands(M, K, N, dev, seed=tp * 7 + S, integers=True)
+    dsts = _receive_buffers(tp, S, N, torch.float32, dev)
+    sp.sp_matmul_scatter(x, w, dsts, rank=tp - 1)
+    x8, w8 = _e4m3_codes((M, K), dev, g), _e4m3_codes((N, K), dev, g)
+    xs = torch.rand((M,), generator=g, device=dev) + 0.5
+    ws = torch.rand((N,), generator=g, device=dev) + 0.5
+    d8 = _receive_buffers(tp, S, N, torch.bfloat16, dev)
+    sp.sp_scaled_matmul_scatter(x8, xs, w8, ws, d8, rank=0)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_scatter(to_host(x), to_host(w), tp=tp, rank=tp - 1)
+    for r in range(tp):
+        np.testing.assert_array_equal(dsts[r][tp - 1].cpu().numpy(), ref[r][tp - 1])
+    _slots_untouched(dsts, tp - 1)
+    _check_fp8(x8, xs, w8, ws, d8, 0)
+    _slots_untouched(d8, 0)
