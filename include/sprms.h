@@ -15,7 +15,9 @@
  *   residual_out[s][h] = z[s][h]                                         (rounded to act dtype)
  *   y[s][h]  = z[s][h] * rsqrt(mean_h z[s][h]^2 + eps) * w[h] (+ b[h])
  *   out      = y (bf16 / f32), or FP8 e4m3 codes of y / scale with
- *              scale a static per-tensor constant or max_h |y[s][h]| / 448
+ *              scale a static per-tensor constant or max_h |y[s][h]| / 448,
+ *              or block-scaled e4m3 / e2m1 codes with one E8M0 scale per
+ *              32 elements
  *   rows s >= valid_rows: residual_out, out and out_scale are 0; their
  *              inputs are not read.
  *
@@ -24,6 +26,19 @@
  * (LongCat-Flash on Atlas A3, openrokid.csdn.net, "o_proj TP K-axis split").
  * One rank's input is emulated as partials[tp][S][H]: the slice
  * [r*S, (r+1)*S) of every rank's partial GEMM output.
+ *
+ * Around that call the library has the other steps of the same tail, each
+ * one kernel, each for one rank's share or for every rank of a group held
+ * on one GPU:
+ *   sp_matmul_scatter, sp_scaled_matmul_scatter -- the producer: a rank's
+ *       row-parallel GEMM (bf16, or e4m3 with scales) writing each token
+ *       block into its destination rank's partials buffer;
+ *   sp_all_gather_unpad -- the AllGather + unpad that follows the shard;
+ *   sp_fc2_regroup, sp_dsacp_heads_to_tokens -- the two regroupings in front
+ *       of o_proj (FlashComm2's ODP all-to-all, DSA-CP's head-to-token
+ *       exchange);
+ *   sp_shard_geometry, sp_validate, sp_error_string, sp_last_error -- host
+ *       helpers.
  *
  * All entry points are plain C; pointers named "device" are HIP device
  * pointers (e.g. torch tensor data_ptr() on a ROCm build), everything else
@@ -66,8 +81,9 @@ typedef enum {
   SP_ERR_NULL = -1,        /* a required pointer is NULL */
   SP_ERR_SHAPE = -2,       /* inconsistent sizes, rank or row counts */
   SP_ERR_DTYPE = -3,       /* unsupported dtype combination */
-  SP_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
-  SP_ERR_UNSUPPORTED = -5, /* unknown quant mode (includes dynamic per-tensor) */
+  SP_ERR_ALIGN = -4,       /* a device pointer is not aligned as the call requires */
+  SP_ERR_UNSUPPORTED = -5, /* a quant mode (dynamic per-tensor included), flag or reserved
+                              field the call does not support */
   SP_ERR_HIP = -6          /* the kernel launch failed */
 } sp_status;
 

@@ -11,9 +11,9 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-# the fused shard kernel, the layout kernels (gather, regroupings) and the
-# producer GEMM
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("sprms.hip", "layout.hip", "gemm.hip")]
+# the fused shard kernel, the layout kernels (gather, regroupings), the
+# producer GEMM, and the host-only C ABI helpers
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("sprms.hip", "layout.hip", "gemm.hip", "abi.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsprms.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
