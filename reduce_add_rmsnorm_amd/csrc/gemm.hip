@@ -14,8 +14,11 @@
 // the 312 flop/B ridge of 2.5 PFLOP/s over 8 TB/s):
 //   * one workgroup of 8 wavefronts per 256 x 256 output tile, two
 //     wavefronts per SIMD so that one issues MFMAs while the other waits on
-//     LDS or a barrier; each wavefront owns 128 columns x 64 tokens as 4 x 2
-//     blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane);
+//     LDS or a barrier; each wavefront owns 128 columns x 64 tokens (128 fp32
+//     accumulators per lane): bf16 as 8 x 4 blocks of
+//     v_mfma_f32_16x16x32_bf16 (measured ~4% faster than 4 x 2 blocks of the
+//     32x32x16 form with the same LDS traffic), e4m3 as 4 x 2 blocks of
+//     v_mfma_scale_f32_32x32x64_f8f6f4;
 //   * the weight tile is the MFMA's A operand and the token tile its B
 //     operand, so each lane's accumulators are 4-element runs of one token
 //     row's output columns;
@@ -66,7 +69,6 @@ constexpr int kXcds = 8;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct MArgs {
@@ -101,16 +103,26 @@ __device__ __forceinline__ void tile_of(const MArgs& a, int* tm, int* tn) {
 // physical 16-byte chunk of logical chunk c in LDS row `row`
 __device__ __forceinline__ int swizzle(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-// IN: SP_BF16 (v_mfma_f32_32x32x16_bf16, K 16 a step) or SP_FP8_E4M3
+// IN: SP_BF16 (v_mfma_f32_16x16x32_bf16, K 32 a step) or SP_FP8_E4M3
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales, K 64 a step,
 // the input scales applied in the epilogue).  Either way an LDS row is 128
 // bytes per stage: 64 bf16 or 128 e4m3 elements of K.
+//
+// Block geometry (BLK = 16 or 32 rows and columns per MFMA block): lane l
+// reads operand row l % BLK of each block, and the 64 / BLK lane groups split
+// the step's K chunks among them; accumulator element 4g + c of block (i, j)
+// is output column BLK*i + 8g + 4*(l / BLK) + c of token BLK*j + l % BLK
+// (g < BLK * BLK / 256).
 template <int OUT, int IN>
 __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a) {
   constexpr bool fp8 = IN == SP_FP8_E4M3;
   constexpr int E = fp8 ? 1 : 2;                 // input bytes per element
   constexpr int BK = kBK * 2 / E;                // K elements per stage
-  constexpr int KSTEP = fp8 ? 64 : 16;           // K elements per MFMA
+  constexpr int KSTEP = fp8 ? 64 : 32;           // K elements per MFMA
+  constexpr int BLK = fp8 ? 32 : 16;             // MFMA block rows / columns
+  constexpr int NI = 128 / BLK, NJ = 64 / BLK;   // blocks per wavefront: columns x tokens
+  constexpr int RUNS = BLK * BLK / 256;          // 4-column runs per lane and block: 1 or 4
+  typedef float Acc __attribute__((ext_vector_type(BLK * BLK / 64)));
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   int tm, tn;
   tile_of(a, &tm, &tn);
@@ -144,25 +156,27 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
     }
   };
 
-  f32x16 acc[4][2];
+  Acc acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < BLK * BLK / 64; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = (a.K + BK - 1) / BK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // operand rows of this lane: row l%32 of each 32-row block, K half l/32
-  // of each MFMA step (bf16: one 16-byte chunk; e4m3: two)
-  const int arow = wn * 128 + (lane & 31), brow = wm * 64 + (lane & 31);
-  const int khalf = lane >> 5;
-  constexpr int kChunks = KSTEP * E / 16 / 2;    // chunks per lane and step: 1 or 2
+  // operand rows of this lane: row l % BLK of each block; lane group l / BLK
+  // takes its share of each MFMA step's K chunks (bf16: one 16-byte chunk;
+  // e4m3: two)
+  const int arow = wn * 128 + lane % BLK, brow = wm * 64 + lane % BLK;
+  const int kgrp = lane / BLK;
+  constexpr int kStepChunks = KSTEP * E / 16;            // 16-byte chunks per MFMA step
+  constexpr int kChunks = kStepChunks / (64 / BLK);      // chunks per lane and step: 1 or 2
   auto frag = [&](const char* op, int r, int ks) {
-    const int c = ks * 2 * kChunks + khalf * kChunks;
+    const int c = ks * kStepChunks + kgrp * kChunks;
     if constexpr (fp8) {
       const u32x4 lo = *reinterpret_cast<const u32x4*>(op + r * 128 + swizzle(r, c) * 16);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(op + r * 128 + swizzle(r, c + 1) * 16);
@@ -182,21 +196,21 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
     const char* sx = sw + kOpBytes;
 #pragma unroll
     for (int ks = 0; ks < BK / KSTEP; ++ks) {
-      Frag fa[4], fb[2];
+      Frag fa[NI], fb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag(sw, arow + i * 32, ks);
+      for (int i = 0; i < NI; ++i) fa[i] = frag(sw, arow + i * BLK, ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = frag(sx, brow + j * 32, ks);
+      for (int j = 0; j < NJ; ++j) fb[j] = frag(sx, brow + j * BLK, ks);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           if constexpr (fp8) {
             // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 code 127)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
                                                                          127, 0, 127);
           } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
           }
         }
     }
@@ -205,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   }
 
   // Epilogue: acc[i][j][4g + c] is output (token ml, column nl + c) with
-  // ml = wm*64 + 32j + l%32, nl = wn*128 + 32i + 8g + 4*(l/32).  The rounded
+  // ml = wm*64 + BLK*j + l%BLK, nl = wn*128 + BLK*i + 8g + 4*(l/BLK).  The rounded
   // tile goes through LDS (bf16: all 256 rows at once; f32: 128 rows per
   // pass), then each token row leaves as 16 bytes per lane.
   constexpr int esz = OUT == SP_F32 ? 4 : 2;
@@ -216,8 +230,8 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   for (int pass = 0; pass < kBM / rows_per_pass; ++pass) {
     if (pass > 0) __syncthreads();  // the previous pass's rows have been read
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ml = wm * 64 + j * 32 + (lane & 31) - pass * rows_per_pass;
+    for (int j = 0; j < NJ; ++j) {
+      const int ml = wm * 64 + j * BLK + lane % BLK - pass * rows_per_pass;
       if (ml < 0 || ml >= rows_per_pass) continue;
       float sx = 1.0f;
       if constexpr (fp8) {  // token scale; rows past M (not stored) read entry 0
@@ -225,10 +239,10 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
         sx = a.x_scale[a.x_scale_rows == 1 || m >= a.M ? 0 : m];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nl = wn * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+        for (int g = 0; g < RUNS; ++g) {
+          const int nl = wn * 128 + i * BLK + g * 8 + (lane / BLK) * 4;
           float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if constexpr (fp8) {  // column scales; columns past N (not stored) read entry 0
