@@ -198,6 +198,14 @@ def _same_device(*tensors):
     return dev
 
 
+def _stream_handle(device, stream):
+    """hipStream_t of `stream` (a torch stream or a raw int handle); torch's
+    current stream on `device` when None."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
 def _check(status: int):
     if status != SP_OK:
         raise SprmsError(status, sp_last_error())
@@ -232,6 +240,64 @@ def make_problem(partials, residual, out, *, tp_rank: int, num_tokens: int, deep
                       partial_scale=partial_scale)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_fused_sizes(partials, residual, weight, bias, quant_mode, deepstack, out, out_scale, *,
+                       tp_rank, num_tokens, residual_out, valid_rows_only, out_dtype):
+    """Tensor sizes against what the kernels will touch.  The C ABI sees only
+    pointers, so this is the one place a buffer that is too small for the
+    descriptor built from `partials` is caught; int addresses are taken as
+    given."""
+    if partials.dim() != 3:
+        raise ValueError("partials must be [tp, S, H]")
+    tp, S, H = partials.shape
+    rows = max(0, min(S, num_tokens - tp_rank * S)) if valid_rows_only else S
+    act = residual.dtype if isinstance(residual, torch.Tensor) else None
+
+    def rows_h(t, name, min_rows, rows_exact=None):
+        if not isinstance(t, torch.Tensor):
+            return
+        if t.dim() != 2 or t.shape[1] != H:
+            raise ValueError(f"{name} must be [rows, H={H}], got {tuple(t.shape)}")
+        if rows_exact is not None and t.shape[0] not in rows_exact:
+            raise ValueError(f"{name} must have {' or '.join(map(str, rows_exact))} rows, got {t.shape[0]}")
+        if t.shape[0] < min_rows:
+            raise ValueError(f"{name} has {t.shape[0]} rows, the call writes {min_rows}")
+        if act is not None and t.dtype != act:
+            raise ValueError(f"{name} must have the residual's dtype {act}, got {t.dtype}")
+
+    rows_h(residual, "residual", 0, (S, tp * S))
+    if deepstack is not None:
+        rows_h(deepstack, "deepstack", 0, (S, tp * S))
+    if residual_out is not None:
+        rows_h(residual_out, "residual_out", rows)
+    for t, name in ((weight, "weight"), (bias, "bias")):
+        if isinstance(t, torch.Tensor):
+            if t.numel() != H:
+                raise ValueError(f"{name} must hold H={H} elements, got {t.numel()}")
+            if act is not None and t.dtype != act:
+                raise ValueError(f"{name} must have the residual's dtype {act}, got {t.dtype}")
+    if isinstance(out, torch.Tensor):
+        od = _sp_dtype(out.dtype) if out_dtype is None else out_dtype
+        row_bytes = {SP_F32: 4 * H, SP_BF16: 2 * H, SP_FP8_E4M3: H, SP_FP4_E2M1: H // 2}.get(od)
+        if row_bytes is not None:
+            if out.dim() != 2 or out.shape[1] * out.element_size() != row_bytes:
+                raise ValueError(f"out rows must be {row_bytes} bytes (H={H}), got shape {tuple(out.shape)} "
+                                 f"of {out.dtype}")
+            if out.shape[0] < rows:
+                raise ValueError(f"out has {out.shape[0]} rows, the call writes {rows}")
+    if isinstance(out_scale, torch.Tensor):
+        if quant_mode in (SP_QUANT_STATIC_TENSOR, SP_QUANT_DYNAMIC_TOKEN):
+            need = 1 if quant_mode == SP_QUANT_STATIC_TENSOR else rows
+            if out_scale.dtype != torch.float32 or out_scale.numel() < need:
+                raise ValueError(f"out_scale must be float32 with at least {need} elements, got "
+                                 f"{out_scale.numel()} of {out_scale.dtype}")
+        elif quant_mode == SP_QUANT_MX_BLOCK and _nbytes(out_scale) < rows * (H // 32):
+            raise ValueError(f"out_scale must hold {rows} x {H // 32} E8M0 bytes, got {_nbytes(out_scale)}")
+
+
 def _partials_addr(partials) -> int:
     _partials_stride(partials)
     return partials.data_ptr()
@@ -256,18 +322,19 @@ def sp_reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, dee
     current stream on partials' device).
     """
     lib = load()
+    _check_fused_sizes(partials, residual, weight, bias, quant_mode, deepstack, out, out_scale,
+                       tp_rank=tp_rank, num_tokens=num_tokens, residual_out=residual_out,
+                       valid_rows_only=valid_rows_only, out_dtype=out_dtype)
     _same_device(partials, residual, weight, bias, deepstack, out, out_scale, residual_out)
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out,
                         valid_rows_only=valid_rows_only, out_dtype=out_dtype,
                         partial_scale=partial_scale)
     with torch.cuda.device(partials.device):
-        if stream is None:
-            stream = torch.cuda.current_stream(partials.device)
-        handle = stream if isinstance(stream, int) else stream.cuda_stream
         _check(lib.sp_reduce_add_rmsnorm(C.byref(prob), _partials_addr(partials), _addr(residual),
                                          _addr(weight), _addr(bias), float(eps), int(quant_mode),
-                                         _addr(deepstack), _addr(out), _addr(out_scale), handle))
+                                         _addr(deepstack), _addr(out), _addr(out_scale),
+                                         _stream_handle(partials.device, stream)))
 
 
 def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, out_scale, *,
@@ -277,16 +344,17 @@ def prepare(partials, residual, weight, bias, eps, quant_mode, deepstack, out, o
     no-argument callable that enqueues the call again (for timing loops).
     The tensors must stay alive and in place while the callable is used."""
     lib = load()
+    _check_fused_sizes(partials, residual, weight, bias, quant_mode, deepstack, out, out_scale,
+                       tp_rank=tp_rank, num_tokens=num_tokens, residual_out=residual_out,
+                       valid_rows_only=valid_rows_only, out_dtype=out_dtype)
     _same_device(partials, residual, weight, bias, deepstack, out, out_scale, residual_out)
     prob = make_problem(partials, residual, out, tp_rank=tp_rank, num_tokens=num_tokens,
                         deepstack=deepstack, residual_out=residual_out,
                         valid_rows_only=valid_rows_only, out_dtype=out_dtype,
                         partial_scale=partial_scale)
-    if stream is None:
-        stream = torch.cuda.current_stream(partials.device)
-    handle = stream if isinstance(stream, int) else stream.cuda_stream
     args = (C.byref(prob), _partials_addr(partials), _addr(residual), _addr(weight), _addr(bias),
-            float(eps), int(quant_mode), _addr(deepstack), _addr(out), _addr(out_scale), handle)
+            float(eps), int(quant_mode), _addr(deepstack), _addr(out), _addr(out_scale),
+            _stream_handle(partials.device, stream))
     fn = lib.sp_reduce_add_rmsnorm
 
     def launch():
@@ -308,10 +376,24 @@ def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int
     for t in shards:
         if t.shape != (S, W) or t.dtype != shards[0].dtype:
             raise ValueError("all shards must share shape and dtype")
+    if out.dim() != 2 or out.shape[1] * out.element_size() != W * shards[0].element_size():
+        raise ValueError(f"out rows must be as wide as the shards' ({W} x {shards[0].dtype})")
+    rows = num_tokens if 0 <= num_tokens <= tp * S else 0   # other counts: the library's error
+    if out.shape[0] < rows:
+        raise ValueError(f"out has {out.shape[0]} rows, the call writes {rows}")
+    srow = 0
+    if shard_scales is not None:
+        if len(shard_scales) != tp:
+            raise ValueError("one scale tensor per shard")
+        sb = _nbytes(shard_scales[0])
+        if any(_nbytes(t) != sb for t in shard_scales) or (S and sb % S):
+            raise ValueError("every shard's scales must be [S, row] of one size")
+        srow = sb // max(S, 1)
+        if isinstance(out_scale, torch.Tensor) and _nbytes(out_scale) < rows * srow:
+            raise ValueError(f"out_scale must hold {rows} x {srow} bytes")
     _same_device(shards, shard_scales, out, out_scale)
     dt = _sp_dtype(shards[0].dtype) if dtype is None else dtype
     H = 2 * W if dt == SP_FP4_E2M1 else W
-    srow = 0 if shard_scales is None else shard_scales[0].nbytes // max(S, 1)
     g = sp_gather_problem(tp=tp, dtype=dt, shard_rows=S, hidden=H, num_tokens=num_tokens,
                           scale_row_bytes=srow)
     src = (C.c_void_p * tp)(*[_addr(t) for t in shards])
@@ -319,16 +401,8 @@ def sp_all_gather_unpad(shards, shard_scales, out, out_scale, *, num_tokens: int
     if shard_scales is not None:
         ssrc = (C.c_void_p * tp)(*[_addr(t) for t in shard_scales])
     with torch.cuda.device(shards[0].device):
-        if stream is None:
-            stream = torch.cuda.current_stream(shards[0].device)
-        handle = stream if isinstance(stream, int) else stream.cuda_stream
-        _check(lib.sp_all_gather_unpad(C.byref(g), src, ssrc, _addr(out), _addr(out_scale), handle))
-
-
-def _stream_handle(device, stream):
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream if isinstance(stream, int) else stream.cuda_stream
+        _check(lib.sp_all_gather_unpad(C.byref(g), src, ssrc, _addr(out), _addr(out_scale),
+                                       _stream_handle(shards[0].device, stream)))
 
 
 def sp_fc2_regroup(srcs, dsts, *, otp: int, rank: int = -1, stream=None) -> None:
@@ -343,6 +417,9 @@ def sp_fc2_regroup(srcs, dsts, *, otp: int, rank: int = -1, stream=None) -> None
             raise ValueError("all sources must share shape and dtype")
     if len(dsts) != G:
         raise ValueError("one destination per rank")
+    for r, d in enumerate(dsts):  # [N/odp, odp*C]: the same elements as a source
+        if d is not None and (d.dtype != srcs[0].dtype or d.numel() != N * Cc):
+            raise ValueError(f"dsts[{r}] must hold {N * Cc} elements of {srcs[0].dtype}")
     _same_device(srcs, dsts)
     f = sp_fc2_problem(global_tp=G, otp=otp, dtype=_sp_dtype(srcs[0].dtype), rank=rank,
                        tokens=N, cols=Cc)
@@ -365,6 +442,9 @@ def sp_dsacp_heads_to_tokens(attn, outs, *, rank: int = -1, stream=None) -> None
             raise ValueError("all inputs must share shape and dtype")
     if W % tp or len(outs) != tp:
         raise ValueError("row width must be tp*D and there must be one output per rank")
+    for q, o in enumerate(outs):  # [tp*S, D]
+        if o is not None and (o.dtype != attn[0].dtype or o.shape != (tp * S, W // tp)):
+            raise ValueError(f"outs[{q}] must be [{tp * S}, {W // tp}] of {attn[0].dtype}")
     _same_device(attn, outs)
     f = sp_dsacp_problem(tp=tp, dtype=_sp_dtype(attn[0].dtype), rank=rank, reserved=0,
                          shard_rows=S, head_cols=W // tp)
