@@ -2,8 +2,8 @@
 arithmetic, so rows whose byte offset from the buffer start exceeds 2^32
 must come out as right as the first rows.  Each case places sampled rows on
 both sides of that boundary and checks them against the oracle (fused call,
-producer GEMM) or byte for byte (gather), with the sizes a 288 GB part holds
-easily (about 12 GB of device memory per case)."""
+producer GEMM, the two regroupings) or byte for byte (gather), with sizes a
+288 GB part holds easily (10-18 GB of device memory per case)."""
 
 import dataclasses
 
@@ -112,4 +112,52 @@ def test_gather_rows_past_4gib(dev):
     assert bool((out_buf[T] == 0x5A).all()) and float(osc_buf[T]) == -1.0, "written past row T"
     say(f"  ok: {len(rows)} rows, {sum(r >= first_high for r in rows)} of them past 4 GiB")
     del shards, scales, out_buf, osc_buf
+    torch.cuda.empty_cache()
+
+
+def test_fc2_regroup_past_4gib(dev):
+    """FlashComm2 regrouping of G=2 ranks (otp=1, odp=2) with 4.4 GB sources
+    and destinations, every rank's destination at once, against the oracle."""
+    G, N, Cc = 2, 1_080_000, 2048
+    assert N * Cc * 2 > GiB4
+    say(f"FC2 regroup past 4 GiB: G={G} otp=1 N={N} C={Cc} bf16")
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    srcs = [torch.randint(-30000, 30000, (N, Cc), generator=g, device=dev, dtype=torch.int16).view(torch.bfloat16)
+            for _ in range(G)]
+    dsts = [torch.empty((N // 2, 2 * Cc), dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    sp.sp_fc2_regroup(srcs, dsts, otp=1)
+    torch.cuda.synchronize()
+    want = oracle.fc2_regroup([to_host(t) for t in srcs], 1)
+    first_high = -(-GiB4 // (2 * Cc * 2))
+    rows = spread(16, 32, first_high, first_high, N // 2, seed=6)
+    idx = torch.tensor(rows, device=dev)
+    for r in range(G):
+        np.testing.assert_array_equal(to_host(dsts[r][idx]), want[r][rows], err_msg=f"rank {r}")
+    say(f"  ok: {len(rows)} rows of each destination, rows >= {first_high} past 4 GiB")
+    del srcs, dsts, want
+    torch.cuda.empty_cache()
+
+
+def test_dsacp_exchange_past_4gib(dev):
+    """DSA-CP head-to-token exchange of tp=2 ranks with 4.4 GB inputs and
+    outputs, against the oracle."""
+    tp, S, D = 2, 1_080_000, 1024
+    assert S * tp * D * 2 > GiB4
+    say(f"DSA-CP exchange past 4 GiB: tp={tp} S={S} D={D} bf16")
+    g = torch.Generator(device=dev)
+    g.manual_seed(24)
+    attn = [torch.randint(-30000, 30000, (S, tp * D), generator=g, device=dev, dtype=torch.int16).view(torch.bfloat16)
+            for _ in range(tp)]
+    outs = [torch.empty((tp * S, D), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+    sp.sp_dsacp_heads_to_tokens(attn, outs)
+    torch.cuda.synchronize()
+    want = oracle.dsacp_heads_to_tokens([to_host(t) for t in attn])
+    first_high = -(-GiB4 // (D * 2))
+    rows = spread(16, 32, first_high, first_high, tp * S, seed=7)
+    idx = torch.tensor(rows, device=dev)
+    for q in range(tp):
+        np.testing.assert_array_equal(to_host(outs[q][idx]), want[q][rows], err_msg=f"rank {q}")
+    say(f"  ok: {len(rows)} rows of each output, rows >= {first_high} past 4 GiB")
+    del attn, outs, want
     torch.cuda.empty_cache()
