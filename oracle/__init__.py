@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     QUANT_MX_BLOCK,
     QUANT_NONE,
     QUANT_STATIC_TENSOR,
+    AbiProblem,
     OracleError,
     all_gather_unpad,
     bf16_from_double,
@@ -33,4 +34,5 @@ from .oracle import (  # noqa: F401
     reduce_add_rmsnorm,
     scaled_matmul_scatter,
     shard_geometry,
+    sp_oracle_reduce_add_rmsnorm,
 )

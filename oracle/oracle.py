@@ -48,6 +48,27 @@ class _Problem(C.Structure):
     ]
 
 
+class AbiProblem(C.Structure):
+    """The descriptor of sp_oracle_reduce_add_rmsnorm: the library
+    descriptor's field layout, defined here on its own."""
+    _fields_ = [
+        ("tp", C.c_int32),
+        ("tp_rank", C.c_int32),
+        ("shard_rows", C.c_int64),
+        ("hidden", C.c_int64),
+        ("num_tokens", C.c_int64),
+        ("partial_dtype", C.c_int32),
+        ("act_dtype", C.c_int32),
+        ("out_dtype", C.c_int32),
+        ("residual_rows", C.c_int64),
+        ("deepstack_rows", C.c_int64),
+        ("residual_out", C.c_void_p),
+        ("partial_stride", C.c_int64),
+        ("flags", C.c_int32),
+        ("partial_scale", C.c_float),
+    ]
+
+
 def build() -> str:
     """Compile the oracle with gcc (always; used by the repository build step)."""
     subprocess.run(GCC_CMD, check=True)
@@ -72,6 +93,9 @@ def _load():
         C.POINTER(_Problem), vp, vp, vp, vp, C.c_float, i32, vp, C.c_float, i64, vp, vp, vp,
         vp, vp, vp]
     lib.orc_reduce_add_rmsnorm.restype = C.c_int
+    lib.sp_oracle_reduce_add_rmsnorm.argtypes = [C.POINTER(AbiProblem), vp, vp, vp, vp, C.c_float,
+                                                 C.c_int, vp, vp, vp, vp]
+    lib.sp_oracle_reduce_add_rmsnorm.restype = C.c_int
     lib.orc_bf16_from_double.argtypes = [C.c_double]
     lib.orc_bf16_from_double.restype = C.c_uint16
     lib.orc_bf16_to_double.argtypes = [C.c_uint16]
@@ -186,6 +210,17 @@ def reduce_add_rmsnorm(partials, residual, weight, bias, eps, quant_mode, deepst
     if quant_mode in (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK):
         result["out_scale"] = scale
     return result
+
+
+def sp_oracle_reduce_add_rmsnorm(problem: AbiProblem, partials, residual, weight, bias, eps,
+                                 quant_mode, deepstack, out, out_scale) -> int:
+    """The fused call with the library entry point's arguments, on host
+    arrays (written in place: out, out_scale, problem.residual_out or the
+    residual).  Returns the C status code."""
+    lib = _load()
+    return lib.sp_oracle_reduce_add_rmsnorm(C.byref(problem), _ptr(partials), _ptr(residual),
+                                            _ptr(weight), _ptr(bias), float(eps), int(quant_mode),
+                                            _ptr(deepstack), _ptr(out), _ptr(out_scale), None)
 
 
 def bf16_from_double(x: float) -> int:

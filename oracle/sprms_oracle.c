@@ -390,6 +390,69 @@ void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_from_double(x[i]);
 }
 
+/* ------------------------------------------ the boundary's argument list */
+
+int sp_oracle_reduce_add_rmsnorm(const orc_abi_problem* a, const void* partials, void* residual,
+                                 const void* weight, const void* bias, float eps, int quant_mode,
+                                 const void* deepstack, void* out, void* out_scale, void* stream) {
+  (void)stream;
+  if (!a) return ORC_ERR_NULL;
+  if (a->flags & ~1) return ORC_ERR_UNSUPPORTED;
+  const orc_problem p = {a->tp, a->tp_rank, a->shard_rows, a->hidden, a->num_tokens,
+                         a->partial_dtype, a->act_dtype, a->out_dtype, a->residual_rows,
+                         a->deepstack_rows, a->partial_scale == 0.0f ? 1.0 : (double)a->partial_scale};
+  const int64_t S = a->shard_rows, H = a->hidden, tp = a->tp;
+  if (tp < 1 || S < 0 || H < 1) return ORC_ERR_SHAPE;
+  if (S == 0) return ORC_OK;
+  if (!residual || !out) return ORC_ERR_NULL;
+  float static_scale = 1.0f;
+  if (quant_mode == ORC_QUANT_STATIC_TENSOR) {
+    if (!out_scale) return ORC_ERR_NULL;
+    static_scale = ((const float*)out_scale)[0];
+  }
+  const int dyn = quant_mode == ORC_QUANT_DYNAMIC_TOKEN, blk = quant_mode == ORC_QUANT_MX_BLOCK;
+  if ((dyn || blk) && !out_scale) return ORC_ERR_NULL;
+  const size_t pe = elt_size(a->partial_dtype), az = elt_size(a->act_dtype);
+  const size_t orow = row_bytes(a->out_dtype, H);
+  if (!pe || !az || !orow) return ORC_ERR_DTYPE;
+  const int64_t stride = a->partial_stride ? a->partial_stride : S * H;
+  if (stride < S * H) return ORC_ERR_SHAPE;
+
+  /* a strided set of partials is packed into [tp][S][H] first */
+  void* packed = NULL;
+  if (partials && stride != S * H) {
+    packed = malloc((size_t)(tp * S * H) * pe);
+    if (!packed) return ORC_ERR_NULL;
+    for (int64_t q = 0; q < tp; ++q)
+      memcpy((char*)packed + (size_t)(q * S * H) * pe, (const char*)partials + (size_t)(q * stride) * pe,
+             (size_t)(S * H) * pe);
+  }
+  const size_t srow = blk ? (size_t)(H / 32) : 4;
+  void* res_t = malloc((size_t)(S * H) * az);
+  void* out_t = malloc((size_t)S * orow);
+  void* sc_t = malloc((size_t)S * srow);
+  int rc = ORC_ERR_NULL;
+  if (res_t && out_t && sc_t)
+    rc = orc_reduce_add_rmsnorm(&p, packed ? packed : partials, residual, weight, bias, eps,
+                                quant_mode, deepstack, static_scale, S, NULL, res_t, out_t,
+                                (dyn || blk) ? sc_t : NULL, NULL, NULL);
+  if (rc == ORC_OK) {
+    int64_t v = a->num_tokens - (int64_t)a->tp_rank * S;
+    v = v < 0 ? 0 : (v > S ? S : v);
+    const int64_t n = (a->flags & 1) ? v : S;  /* rows written */
+    const int64_t roff = (a->residual_rows == tp * S && tp > 1) ? (int64_t)a->tp_rank * S : 0;
+    void* res_dst = a->residual_out ? a->residual_out : (char*)residual + (size_t)(roff * H) * az;
+    memcpy(res_dst, res_t, (size_t)(n * H) * az);
+    memcpy(out, out_t, (size_t)n * orow);
+    if (dyn || blk) memcpy(out_scale, sc_t, (size_t)n * srow);
+  }
+  free(packed);
+  free(res_t);
+  free(out_t);
+  free(sc_t);
+  return rc;
+}
+
 /* ------------------------------------------------------- all-gather + unpad */
 
 /* AllGather followed by unpad ([SP/FC] §3.3: gather the shards along the

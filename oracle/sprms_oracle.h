@@ -89,6 +89,38 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
                            void* residual_out, void* out, void* out_scale,
                            double* z_dbg, double* y_dbg);
 
+/* The fused call with the library boundary's own argument list, on host
+ * memory: the descriptor below has the field layout of the library's
+ * problem descriptor (written out here on its own: the oracle includes no
+ * header of the library) and the arguments follow the library entry point,
+ * so a caller can hand the same call to both.  The stream is ignored.
+ * Semantics on top of orc_reduce_add_rmsnorm:
+ *   residual_out NULL      the residual rows this shard uses (block tp_rank of a
+ *                          replicated residual) are overwritten in place;
+ *   partial_stride         elements from partial q's row s to partial q+1's
+ *                          row s; 0 means S*H (packed);
+ *   flags bit 0            outputs for the valid rows only, padding rows of
+ *                          out / residual_out / out_scale untouched;
+ *   partial_scale          0 is read as 1;
+ *   out_scale              static: [1] read; dynamic: [S] f32 written; block:
+ *                          [S][H/32] E8M0 bytes written.
+ * Every output is computed before the first write, so a call that returns
+ * an error has written nothing. */
+typedef struct {
+  int32_t tp, tp_rank;
+  int64_t shard_rows, hidden, num_tokens;
+  int32_t partial_dtype, act_dtype, out_dtype;
+  int64_t residual_rows, deepstack_rows;
+  void* residual_out;
+  int64_t partial_stride;
+  int32_t flags;
+  float partial_scale;
+} orc_abi_problem;
+
+int sp_oracle_reduce_add_rmsnorm(const orc_abi_problem* p, const void* partials, void* residual,
+                                 const void* weight, const void* bias, float eps, int quant_mode,
+                                 const void* deepstack, void* out, void* out_scale, void* stream);
+
 /* AllGather + unpad of tp shard outputs of S rows (row_bytes each) into out
  * of T rows; shard scales of S rows (scale_row_bytes each) into out_scale of T
  * rows when scales != NULL (scale_row_bytes 0 otherwise). */
