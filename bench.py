@@ -250,8 +250,12 @@ def library_gemm_us(x, wt, steps=20):
     return e0.elapsed_time(e1) * 1000 / steps
 
 
-def cpu_baseline(w, x, budget_s: float):
-    """The C oracle on the first rows of the same shard, single-threaded."""
+def cpu_baseline(w, x, budget_s: float, threads: int):
+    """The C oracle on the first rows of the same shard: single-threaded, then
+    the same code on disjoint row chunks in `threads` threads at once (the
+    oracle's C call releases the interpreter lock)."""
+    import threading
+
     import oracle  # CPU checker; only this leg of the benchmark uses it
 
     def bits(t):
@@ -262,29 +266,46 @@ def cpu_baseline(w, x, budget_s: float):
     r = w.rank
     roff = r * S if w.residual_replicated else 0
 
-    def sample(n):
-        P = bits(x["partials"][:, :n])
-        R = bits(x["residual"][roff:roff + n])
-        D = None if x["deepstack"] is None else bits(x["deepstack"][r * S:r * S + n])
+    def sample(a, b):
+        """Rows [a, b) of the shard as a compact shard of their own (every row valid)."""
+        P = bits(x["partials"][:, a:b])
+        R = bits(x["residual"][roff + a:roff + b])
+        D = None if x["deepstack"] is None else bits(x["deepstack"][r * S + a:r * S + b])
         wt = bits(x["weight"])
-        b = None if x["bias"] is None else bits(x["bias"])
-        return P, R, D, wt, b
+        bias = None if x["bias"] is None else bits(x["bias"])
+        return P, R, D, wt, bias
 
-    def run(n):
-        P, R, D, wt, b = sample(n)
-        t0 = time.perf_counter()
-        oracle.reduce_add_rmsnorm(P, R, wt, b, w.eps, w.quant_mode, D, tp_rank=r,
-                                  num_tokens=w.tp * n,
+    def call(arrays):
+        P, R, D, wt, bias = arrays
+        oracle.reduce_add_rmsnorm(P, R, wt, bias, w.eps, w.quant_mode, D, tp_rank=r,
+                                  num_tokens=w.tp * P.shape[1],
                                   out_dtype=oracle.ORC_E2M1 if w.fp4 else oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
                                   else oracle.ORC_E4M3,
                                   static_scale=static_scale() if w.quant_mode == QUANT_STATIC_TENSOR
                                   else 1.0, want_debug=False)
+
+    def run(n):
+        arrays = sample(0, n)
+        t0 = time.perf_counter()
+        call(arrays)
         return time.perf_counter() - t0
 
     t_probe = run(8) / 8
     n = int(min(S, max(8, budget_s / max(t_probe, 1e-9))))
     secs = run(n)
     per_row = w.algorithmic_bytes() / S  # all rows valid in the timed workloads
+
+    # the same code on all host threads: disjoint row chunks, one call each
+    n_par = int(min(S, max(threads, threads * budget_s / (secs / n))))
+    bounds = np.linspace(0, n_par, threads + 1).astype(int)
+    chunks = [sample(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    workers = [threading.Thread(target=call, args=(c,)) for c in chunks]
+    t0 = time.perf_counter()
+    for t_ in workers:
+        t_.start()
+    for t_ in workers:
+        t_.join()
+    par_secs = time.perf_counter() - t0
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -300,6 +321,11 @@ def cpu_baseline(w, x, budget_s: float):
                   f"{n / secs:.1f} shard tokens/s",
         "tokens_per_s": round(n / secs, 2),
         "seconds": round(secs, 2),
+        "parallel": {"value": round(n_par * per_row / par_secs / 1e9, 4), "unit": "GB/s",
+                     "cores": len(workers), "tokens_per_s": round(n_par / par_secs, 2),
+                     "seconds": round(par_secs, 2),
+                     "sample": f"first {n_par} of {S} rows in {len(workers)} disjoint chunks, "
+                               f"one thread each"},
         "host": {"cpu": model, "logical_cpus": os.cpu_count()},
     }
 
@@ -329,7 +355,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C5", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of single-thread oracle work for the CPU baseline (0: skip)")
+                    help="seconds of oracle work for each leg of the CPU baseline, single "
+                         "thread and all threads (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16),
+                    help="threads of the parallel CPU-baseline leg (default: the host's, at most 16)")
+    ap.add_argument("--cold", action="store_true",
+                    help="cache-cold protocol for shards that fit the 256 MB Infinity Cache: "
+                         "a 512 MiB read+write scrub before every launch, each launch timed "
+                         "by its own event pair, value from the median launch")
     ap.add_argument("--path", default="fused", choices=["fused", "gather", "fc2", "dsacp", "gemm"],
                     help="fused: the shard kernel (the headline); gather: AllGather + unpad of "
                          "every rank's shard output of the workload into [T, H] on this GPU; "
@@ -393,32 +426,48 @@ def main():
         launch()
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back launches, HIP events on the launch stream
-    # at both ends, host clock between two synchronisations
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_ms = ev0.elapsed_time(ev1) / args.steps
+    if not args.cold:
+        # timed region: K back-to-back launches, HIP events on the launch stream
+        # at both ends, host clock between two synchronisations
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        avg_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # launch-duration spread from a short pass with an event pair per launch
-    n_spread = min(args.steps, 50)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
-    for i in range(n_spread):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
-
-    ms_per_step = wall * 1000.0 / args.steps
+        # launch-duration spread from a short pass with an event pair per launch
+        n_spread = min(args.steps, 50)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+        for i in range(n_spread):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+        ms_per_step = wall * 1000.0 / args.steps
+    else:
+        # cache-cold: before every launch a read+write pass over 512 MiB (twice
+        # the Infinity Cache) on the same stream, outside the launch's events
+        scrub = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scrub.add_(1)
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+        avg_ms = ms_per_step = statistics.median(per_launch_ms)
+        del scrub
     gemm = args.path == "gemm"
     scale = 1e12 if gemm else 1e9   # TFLOP/s for the GEMM, GB/s for the rest
     peak = (MFMA_FP8_PEAK_TFLOPS if fp8_gemm else MFMA_BF16_PEAK_TFLOPS) if gemm else HBM_PEAK_GBS
@@ -457,6 +506,8 @@ def main():
             "quant": QUANT_NAMES[w.quant_mode] + (
                 (" e2m1" if w.fp4 else " e4m3") if w.quant_mode == QUANT_MX_BLOCK else ""),
             "deepstack": w.deepstack, "bias": w.bias,
+            **({"protocol": "cache-cold: 512 MiB read+write scrub before each launch; value and "
+                            "roofline from the median per-launch HIP-event time"} if args.cold else {}),
             ("algorithmic_flops" if gemm else "algorithmic_bytes"): nbytes,
             # the GEMM moves x, w and its output once each
             **({"algorithmic_bytes": (1 if fp8_gemm else 2) * (w.num_tokens_pad * (w.hidden // w.tp)
@@ -467,7 +518,7 @@ def main():
         "pct_of_peak": round(100.0 * value / peak, 2),
         "shard_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
         "kernel_us": {
-            "mean": round(avg_ms * 1000, 2),
+            "mean": round((statistics.mean(per_launch_ms) if args.cold else avg_ms) * 1000, 2),
             "median_single": round(statistics.median(per_launch_ms) * 1000, 2),
             "p10": round(float(np.percentile(per_launch_ms, 10)) * 1000, 2),
             "p90": round(float(np.percentile(per_launch_ms, 90)) * 1000, 2),
@@ -483,7 +534,7 @@ def main():
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0 and args.path == "fused":
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget, max(1, args.cpu_threads))
     if gemm and fp8_gemm:
         result["context"] = {"hipblaslt_scaled_mm_us": library_fp8_gemm_us(x[0], x[1], x[2], x[3]),
                              "note": "torch._scaled_mm (hipBLASLt) on the same codes and scales, "
