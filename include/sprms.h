@@ -129,7 +129,9 @@ typedef struct {
  * contiguous shard, valid-row rule and zeroed padding rows (vllm-ascend
  * PR #18671 walkthrough, §2, §5.2, §5.3).
  *
- * Arguments (device pointers, 16-byte aligned, row-major, no row padding):
+ * Arguments (device pointers, row-major, no row padding; 16-byte aligned except
+ * out, which needs the width of one 8-element store: 16 bytes for bf16 and f32,
+ * 8 for e4m3, 4 for packed e2m1):
  *   p          problem descriptor (host)
  *   partials   [tp][S][H] partial_dtype: partial q's rows of this shard
  *   residual   [residual_rows][H] act_dtype; written in place when

@@ -664,9 +664,15 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
     if (quant_mode != SP_QUANT_NONE && !out_scale)
       return fail(SP_ERR_NULL, "out_scale must be non-NULL with quant_mode=%d", quant_mode);
   }
-  const void* dev[] = {partials, residual, weight, bias, deepstack, out, p->residual_out};
+  const void* dev[] = {partials, residual, weight, bias, deepstack, p->residual_out};
   for (const void* d : dev)
     if (d && misaligned(d)) return fail(SP_ERR_ALIGN, "device pointer %p is not 16-byte aligned", d);
+  // out: the width of one lane's store (8 elements) -- 16 bytes for bf16 and
+  // f32, 8 for e4m3, 4 for packed e2m1 -- so that an e4m3 out may start at any
+  // row of a gathered tensor whose rows are a multiple of 8 bytes
+  const uintptr_t out_align = p->out_dtype == SP_FP8_E4M3 ? 8 : p->out_dtype == SP_FP4_E2M1 ? 4 : 16;
+  if (out && misaligned(out, out_align))
+    return fail(SP_ERR_ALIGN, "out %p is not %d-byte aligned", out, static_cast<int>(out_align));
   const int64_t stride = p->partial_stride ? p->partial_stride : S * H;
   if ((stride * static_cast<int64_t>(elt_size(p->partial_dtype))) % 16 != 0)
     return fail(SP_ERR_ALIGN, "partial_stride=%lld elements is not a multiple of 16 bytes",

@@ -141,6 +141,20 @@ def test_invalid_problems_are_rejected(case, expect):
     assert msg and msg != "no error"
 
 
+def test_out_alignment_is_the_store_width():
+    """out needs the width of one lane's 8-element store: 16 bytes for bf16
+    and f32, 8 for e4m3, 4 for packed e2m1 (MX scale bytes need none)."""
+    fp8 = dict(quant_mode=sp.SP_QUANT_DYNAMIC_TOKEN, out_scale=BASE + 5 * GB)
+    mx = dict(quant_mode=sp.SP_QUANT_MX_BLOCK, out_scale=BASE + 5 * GB + 1)
+    cases = [(sp.SP_BF16, {}, 8, sp.SP_ERR_ALIGN), (sp.SP_F32, {}, 8, sp.SP_ERR_ALIGN),
+             (sp.SP_FP8_E4M3, fp8, 8, sp.SP_OK), (sp.SP_FP8_E4M3, fp8, 4, sp.SP_ERR_ALIGN),
+             (sp.SP_FP8_E4M3, mx, 8, sp.SP_OK), (sp.SP_FP4_E2M1, mx, 4, sp.SP_OK),
+             (sp.SP_FP4_E2M1, mx, 2, sp.SP_ERR_ALIGN), (sp.SP_BF16, {}, 16, sp.SP_OK)]
+    for dt, q, off, want in cases:
+        status, msg = validate(problem(out_dtype=dt), out=BASE + 3 * GB + off, **q)
+        assert status == want, (dt, off, msg)
+
+
 def test_strided_and_valid_rows_only_problems_pass():
     assert validate(problem(partial_stride=1024 * 4096))[0] == sp.SP_OK
     assert validate(problem(flags=sp.SP_FLAG_VALID_ROWS_ONLY))[0] == sp.SP_OK
