@@ -74,9 +74,19 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name, tmp_path):
-    old, new = MUTATIONS[name]
+# mistakes in the entry point with the library's argument list, which
+# tests/test_oracle_abi.py pins to the (unchanged) row-list function
+ABI_MUTATIONS = {
+    "abi_in_place_wrong_block": ("(a->residual_rows == tp * S && tp > 1) ? (int64_t)a->tp_rank * S : 0",
+                                 "(a->residual_rows == tp * S && tp > 1) ? 0 : 0"),
+    "abi_valid_rows_flag_ignored": ("const int64_t n = (a->flags & 1) ? v : S;", "const int64_t n = S;"),
+    "abi_stride_ignored": ("if (partials && stride != S * H) {", "if (0) {"),
+    "abi_static_scale_not_read": ("static_scale = ((const float*)out_scale)[0];", "static_scale = 1.0f;"),
+    "abi_zero_partial_scale_kept": ("a->partial_scale == 0.0f ? 1.0 :", "a->partial_scale == 0.0f ? 0.0 :"),
+}
+
+
+def _caught(name, old, new, pins, tmp_path):
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
     mutated = tmp_path / "oracle_mut.c"
@@ -87,6 +97,16 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                    check=True)
     env = dict(os.environ, SPRMS_ORACLE_LIB=str(lib))
     proc = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           os.path.join(ROOT, "tests", pins)],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert proc.returncode != 0, f"pins did not catch mutation {name}:\n{proc.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(ABI_MUTATIONS))
+def test_abi_pins_catch_planted_mistake(name, tmp_path):
+    _caught(name, *ABI_MUTATIONS[name], "test_oracle_abi.py", tmp_path)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    _caught(name, *MUTATIONS[name], "test_oracle_pins.py", tmp_path)
