@@ -86,9 +86,14 @@ def setup(w, dev):
         scale = torch.empty((S,), dtype=torch.float32, device=dev)
     elif w.quant_mode == QUANT_MX_BLOCK:
         scale = torch.empty((S, H // 32), dtype=torch.uint8, device=dev)
-    launch = sp.prepare(x["partials"], x["residual"], x["weight"], x["bias"], w.eps, w.quant_mode,
-                        x["deepstack"], out, scale, tp_rank=w.rank, num_tokens=w.num_tokens,
-                        residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if w.fp4 else None)
+    def make_launch():
+        """The call marshalled once, on torch's current stream at this moment."""
+        return sp.prepare(x["partials"], x["residual"], x["weight"], x["bias"], w.eps, w.quant_mode,
+                          x["deepstack"], out, scale, tp_rank=w.rank, num_tokens=w.num_tokens,
+                          residual_out=res_out, out_dtype=sp.SP_FP4_E2M1 if w.fp4 else None)
+
+    launch = make_launch()
+    launch.remake = make_launch
     return x, launch, (out, res_out, scale)
 
 
@@ -359,6 +364,9 @@ def main():
                          "thread and all threads (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=min(os.cpu_count() or 1, 16),
                     help="threads of the parallel CPU-baseline leg (default: the host's, at most 16)")
+    ap.add_argument("--graph", type=int, default=0, metavar="N",
+                    help="capture N launches in one HIP graph and time back-to-back replays "
+                         "(per-launch cost without the host launch path, as in a captured step)")
     ap.add_argument("--cold", action="store_true",
                     help="cache-cold protocol for shards that fit the 256 MB Infinity Cache: "
                          "a 512 MiB read+write scrub before every launch, each launch timed "
@@ -426,7 +434,43 @@ def main():
         launch()
     torch.cuda.synchronize()
 
-    if not args.cold:
+    if args.graph and args.cold:
+        ap.error("--graph and --cold are separate protocols")
+    if args.graph:
+        # N launches captured once (side-stream warm-up first, as capture
+        # requires), then ceil(K / N) replays timed by one event pair
+        # a prepared launch holds the stream it was made on: remake it on the
+        # side and capture streams (the other paths read the current stream)
+        remake = getattr(launch, "remake", lambda: launch)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            remake()()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            captured = remake()
+            for _ in range(args.graph):
+                captured()
+        replays = -(-args.steps // args.graph)
+        for _ in range(3):
+            graph.replay()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        n_launch = replays * args.graph
+        avg_ms = ev0.elapsed_time(ev1) / n_launch
+        ms_per_step = wall * 1000.0 / n_launch
+        per_launch_ms = [avg_ms]
+    elif not args.cold:
         # timed region: K back-to-back launches, HIP events on the launch stream
         # at both ends, host clock between two synchronisations
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -508,6 +552,8 @@ def main():
             "deepstack": w.deepstack, "bias": w.bias,
             **({"protocol": "cache-cold: 512 MiB read+write scrub before each launch; value and "
                             "roofline from the median per-launch HIP-event time"} if args.cold else {}),
+            **({"protocol": f"HIP graph of {args.graph} launches, replayed back to back"}
+               if args.graph else {}),
             ("algorithmic_flops" if gemm else "algorithmic_bytes"): nbytes,
             # the GEMM moves x, w and its output once each
             **({"algorithmic_bytes": (1 if fp8_gemm else 2) * (w.num_tokens_pad * (w.hidden // w.tp)
