@@ -1,6 +1,7 @@
-// common.h -- pieces shared by the two translation units of libsprms: the
-// buffer-descriptor row I/O used by every kernel, the size limits, and the
-// host-side error channel and pointer checks behind the C ABI.
+// common.h -- pieces shared by the translation units of libsprms (sprms.hip,
+// layout.hip, gemm.hip, abi.cpp): the buffer-descriptor row I/O used by every
+// kernel, the size limits, and the host-side error channel and pointer checks
+// behind the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

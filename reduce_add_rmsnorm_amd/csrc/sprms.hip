@@ -1,6 +1,7 @@
 // sprms.hip -- libsprms: fused ReduceScatter-reduce + deepstack/residual add +
-// RMSNorm (+bias) + optional FP8 e4m3 quantisation for one rank's token
-// shard, written for MI355X (gfx950, CDNA4).
+// RMSNorm (+bias) + optional output quantisation (e4m3 with a static or
+// per-token scale, or block-scaled MXFP8 / MXFP4) for one rank's token shard,
+// written for MI355X (gfx950, CDNA4).
 //
 // What is computed is stated in include/sprms.h, with the passages of the
 // pages that define it.  This file is the fused kernel family and its
@@ -29,17 +30,17 @@
 //     wavefronts through LDS with one barrier; with a bias the per-token max
 //     needs y, so a second LDS step follows;
 //   * output conversion uses gfx950's v_cvt_pk_bf16_f32 / v_cvt_pk_fp8_f32
-//     (OCP e4m3fn), after an explicit clamp to +-448;
+//     (OCP e4m3fn), after an explicit clamp to +-448; block scaling takes the
+//     32-element max across a quad of lanes (DPP), an E8M0 exponent from
+//     v_frexp_exp, exact v_ldexp scaling and v_cvt_scalef32_pk_fp4_f32 for
+//     e2m1;
 //   * padding rows (s >= valid_rows) only store zeros.
 // Rows are independent and there is no reuse across rows except the gain and
 // bias vectors (a few KiB, served from each XCD's L2), so the workgroup ->
 // row mapping needs no XCD-aware swizzle.
 #include <hip/hip_runtime.h>
 
-#include <stdarg.h>
 #include <stdint.h>
-#include <stdio.h>
-#include <string.h>
 
 #include "common.h"
 #include "sprms.h"
