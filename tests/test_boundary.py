@@ -418,3 +418,35 @@ def test_plain_c_client_compiles_links_and_runs(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
     assert "c abi ok" in out.stdout
+
+
+def test_last_error_is_per_thread():
+    """Calls on several threads at once: each thread reads back the detail of
+    its own last failure (the library keeps no other state across calls)."""
+    import threading
+
+    cases = {
+        "tp": (problem(tp=0), {}),
+        "hidden": (problem(hidden=4100), {}),
+        "quant": (problem(), dict(quant_mode=3)),
+        "align": (problem(), dict(partials=BASE + 8)),
+    }
+    expect = {"tp": "tp=0", "hidden": "hidden=4100", "quant": "quant_mode=3", "align": "aligned"}
+    errors = []
+    barrier = threading.Barrier(len(cases))
+
+    def worker(name):
+        p, kw = cases[name]
+        barrier.wait()
+        for _ in range(200):
+            status, msg = validate(p, **kw)
+            if status == sp.SP_OK or expect[name] not in msg:
+                errors.append((name, status, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
