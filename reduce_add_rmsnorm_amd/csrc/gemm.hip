@@ -23,9 +23,15 @@
 //     operand, so each lane's accumulators are 4-element runs of one token
 //     row's output columns;
 //   * K advances 64 at a time through two LDS stages filled by buffer loads
-//     that write LDS directly (16 bytes per lane, no staging registers): the
-//     loads of step k+1 are issued before step k's MFMAs and waited for
-//     before the barrier that ends the step.  LDS rows are 128 bytes with
+//     that write LDS directly (16 bytes per lane, no staging registers).
+//     bf16 is software-pipelined: a stage's fragments are all in registers
+//     when its step begins, each is refilled from the next stage right after
+//     its last MFMA, and the loads two stages ahead are spread over the
+//     first k-step (~8% faster than reading each k-step's fragments at its
+//     start, which left every wavefront waiting on LDS at each barrier).
+//     e4m3 issues the next stage's loads before the current stage's MFMAs
+//     and reads fragments per k-step (the pipelined form was slower there).
+//     LDS rows are 128 bytes with
 //     their 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 rows an
 //     MFMA operand read touches per 16 lanes land on distinct banks;
 //   * the epilogue stages the rounded tile in LDS and writes each token row
@@ -43,6 +49,8 @@
 
 #include <stdint.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "sprms.h"
@@ -65,6 +73,10 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int kSmemBytes = cmax(2 * kStageBytes, cmax(kBM * out_row_bytes(2), kOutRowsF32 * out_row_bytes(4)));
 constexpr int kGroupM = 4;               // token bands per tile group
 constexpr int kXcds = 8;
+// s_waitcnt operand that waits for lgkmcnt(0) only (vmcnt and expcnt at their maxima)
+constexpr int kLgkmZero = 0xC07F;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -142,18 +154,21 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   // bytes, lane l at byte 16*l, i.e. row l >> 3, physical chunk l & 7; the
   // lane fetches the logical chunk that the swizzle puts there.
   const int grow = lane >> 3, pchunk = lane & 7;
+  // load u (0..7) of the eight a wavefront issues per stage: rows group
+  // wave + 8 * (u / 2) of the weight (u even) or token (u odd) operand
+  auto issue_one = [&](int stage, int kb, int u) {
+    const int g = wave + (kThreads / 64) * (u >> 1);  // group of 8 rows
+    const int row = g * 8 + grow;
+    const int k = kb + swizzle(row, pchunk) * (16 / E);  // first element of the chunk
+    const uint32_t oob = (static_cast<uint32_t>(k - a.K) >> 31) ? 0u : 0x80000000u;
+    const uint32_t off = (static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(k) * E) | oob;
+    char* base = smem + stage * kStageBytes + g * 1024 + (u & 1) * kOpBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds((u & 1) ? gx : gw, (lds_void*)base, 16, off, 0, 0, kCachedPolicy);
+  };
+  constexpr int kLoads = 2 * kBM / 8 / (kThreads / 64);
   auto issue = [&](int stage, int kb) {
 #pragma unroll
-    for (int t = 0; t < kBM / 8 / (kThreads / 64); ++t) {
-      const int g = wave + (kThreads / 64) * t;  // group of 8 rows
-      const int row = g * 8 + grow;
-      const int k = kb + swizzle(row, pchunk) * (16 / E);  // first element of the chunk
-      const uint32_t oob = (static_cast<uint32_t>(k - a.K) >> 31) ? 0u : 0x80000000u;
-      const uint32_t off = (static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(k) * E) | oob;
-      char* base = smem + stage * kStageBytes + g * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(gw, (lds_void*)base, 16, off, 0, 0, kCachedPolicy);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(gx, (lds_void*)(base + kOpBytes), 16, off, 0, 0, kCachedPolicy);
-    }
+    for (int u = 0; u < kLoads; ++u) issue_one(stage, kb, u);
   };
 
   Acc acc[NI][NJ];
@@ -189,33 +204,99 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
     }
   };
   using Frag = decltype(frag(smem, 0, 0));
-  for (int kt = 0; kt < nk; ++kt) {
-    // the next step's loads (past K on the last step: zeros into the idle stage)
-    issue((kt + 1) & 1, (kt + 1) * BK);
-    const char* sw = smem + (kt & 1) * kStageBytes;
-    const char* sx = sw + kOpBytes;
-#pragma unroll
-    for (int ks = 0; ks < BK / KSTEP; ++ks) {
-      Frag fa[NI], fb[NJ];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) fa[i] = frag(sw, arow + i * BLK, ks);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[j] = frag(sx, brow + j * BLK, ks);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if constexpr (fp8) {
-            // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 code 127)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0,
-                                                                         127, 0, 127);
-          } else {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-          }
-        }
+  auto mfma = [&](const Frag& x, const Frag& y, Acc& c) {
+    if constexpr (fp8) {
+      // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 code 127)
+      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+    } else {
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the next stage have landed
-    __syncthreads();
+  };
+  if constexpr (fp8) {
+    // e4m3: each k-step's fragments are read at the start of the step, and
+    // the loads of stage kt + 1 issued ahead of stage kt's MFMAs
+    for (int kt = 0; kt < nk; ++kt) {
+      // the next step's loads (past K on the last step: zeros into the idle stage)
+      issue((kt + 1) & 1, (kt + 1) * BK);
+      const char* sw = smem + (kt & 1) * kStageBytes;
+      const char* sx = sw + kOpBytes;
+#pragma unroll
+      for (int ks = 0; ks < BK / KSTEP; ++ks) {
+        Frag fa[NI], fb[NJ];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) fa[i] = frag(sw, arow + i * BLK, ks);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[j] = frag(sx, brow + j * BLK, ks);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) mfma(fa[i], fb[j], acc[i][j]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the next stage have landed
+      __syncthreads();
+    }
+  } else {
+    // bf16: software-pipelined.  Both k-steps' fragments of stage kt are in
+    // registers when its step starts; during the step every fragment is
+    // refilled from stage kt + 1 as soon as its last MFMA has been issued
+    // (an A row after its NJ MFMAs, the B fragments within the last row),
+    // and the loads of stage kt + 2 go out one per A row of the first
+    // k-step.  The only LDS wait left at a barrier is for the last one or
+    // two reads, where reading all fragments at the start of a step left
+    // every wavefront of the CU waiting for 12 reads at once.  Scheduling
+    // groups keep that order: MFMA, global load, LDS read.
+    static_assert(BK / KSTEP == 2 && kLoads == NI, "two k-steps per stage, one load per A row");
+    Frag fa[NI], fb[NJ], na[NI], nb[NJ];  // k-step 0 and k-step 1 of the current stage
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      fa[i] = frag(smem, arow + i * BLK, 0);
+      na[i] = frag(smem, arow + i * BLK, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      fb[j] = frag(smem + kOpBytes, brow + j * BLK, 0);
+      nb[j] = frag(smem + kOpBytes, brow + j * BLK, 1);
+    }
+    if (nk > 1) issue(1, BK);
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+    // one stage; ISSUE: load stage kt + 2 into stage kt's buffer, NEXT: refill from stage kt + 1
+    auto step = [&](int kt, auto issue_c, auto next_c) {
+      constexpr bool ISSUE = decltype(issue_c)::value, NEXT = decltype(next_c)::value;
+      // stage kt + 1 has landed and every wavefront has read stage kt
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const char* nx = smem + ((kt + 1) & 1) * kStageBytes;
+      auto kstep = [&](Frag* A, Frag* B, int h, auto loads_c) {
+        constexpr bool LOADS = decltype(loads_c)::value;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            mfma(A[i], B[j], acc[i][j]);
+            if (i == NI - 1) {  // the last use of B[j]
+              if constexpr (NEXT) B[j] = frag(nx + kOpBytes, brow + j * BLK, h);
+              __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+              if constexpr (NEXT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+          }
+          if constexpr (LOADS) issue_one(kt & 1, (kt + 2) * BK, i);
+          if constexpr (NEXT) A[i] = frag(nx, arow + i * BLK, h);
+          if (i < NI - 1) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NJ, 0);
+          if constexpr (LOADS) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+          if constexpr (NEXT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+      };
+      kstep(fa, fb, 0, std::integral_constant<bool, ISSUE>{});
+      kstep(na, nb, 1, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step(kt, Yes{}, Yes{});
+    if (kt + 1 < nk) step(kt++, No{}, Yes{});
+    step(kt, No{}, No{});
+    __syncthreads();  // every wavefront is done with the loop's LDS
   }
 
   // Epilogue: acc[i][j][4g + c] is output (token ml, column nl + c) with
