@@ -105,6 +105,9 @@ def _slots_untouched(dsts, rank):
     (2, 300, 136, 520, torch.float32),   # 3 x 3 tiles, ragged M, N and a K tail of 8
     (2, 300, 136, 520, torch.bfloat16),
     (4, 64, 64, 256, torch.bfloat16),    # exactly one tile
+    (2, 70, 128, 264, torch.bfloat16),   # exactly two K stages
+    (1, 40, 72, 136, torch.float32),     # two K stages, the second a tail of 8
+    (2, 130, 192, 256, torch.bfloat16),  # exactly three K stages
     (1, 5, 8, 8, torch.float32),         # smallest
     (8, 33, 896, 1024, torch.bfloat16),  # K of one rank at hidden 7168 over 8 ranks
     (3, 100, 1288, 264, torch.float32),  # long K with a tail, N just past a tile
