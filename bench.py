@@ -255,83 +255,181 @@ def library_gemm_us(x, wt, steps=20):
     return e0.elapsed_time(e1) * 1000 / steps
 
 
-def cpu_baseline(w, x, budget_s: float, threads: int):
-    """The C oracle on the first rows of the same shard: single-threaded, then
-    the same code on disjoint row chunks in `threads` threads at once (the
-    oracle's C call releases the interpreter lock)."""
+def _host_bits(t):
+    """A device tensor as a host array; bf16 as its uint16 bit patterns."""
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _oracle_legs(units: int, make, call, budget_s: float, threads: int):
+    """Time the oracle on units [0, n) of the workload in one thread, n grown
+    from a probe until the leg takes about budget_s; when all units take
+    less, the call is repeated to fill the budget and timed per call.  Then
+    the same code on disjoint unit ranges in `threads` threads at once (the
+    oracle's C calls release the interpreter lock), repeated as often.
+    make(a, b) builds the host arguments of units [a, b) outside the timed
+    region; call runs the oracle on them.  Returns (n, seconds per call,
+    repeats, n_parallel, seconds per parallel round, threads used)."""
     import threading
 
-    import oracle  # CPU checker; only this leg of the benchmark uses it
-
-    def bits(t):
-        t = t.contiguous().cpu()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
-
-    S = w.shard_rows
-    r = w.rank
-    roff = r * S if w.residual_replicated else 0
-
-    def sample(a, b):
-        """Rows [a, b) of the shard as a compact shard of their own (every row valid)."""
-        P = bits(x["partials"][:, a:b])
-        R = bits(x["residual"][roff + a:roff + b])
-        D = None if x["deepstack"] is None else bits(x["deepstack"][r * S + a:r * S + b])
-        wt = bits(x["weight"])
-        bias = None if x["bias"] is None else bits(x["bias"])
-        return P, R, D, wt, bias
-
-    def call(arrays):
-        P, R, D, wt, bias = arrays
-        oracle.reduce_add_rmsnorm(P, R, wt, bias, w.eps, w.quant_mode, D, tp_rank=r,
-                                  num_tokens=w.tp * P.shape[1],
-                                  out_dtype=oracle.ORC_E2M1 if w.fp4 else oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
-                                  else oracle.ORC_E4M3,
-                                  static_scale=static_scale() if w.quant_mode == QUANT_STATIC_TENSOR
-                                  else 1.0, want_debug=False)
-
     def run(n):
-        arrays = sample(0, n)
+        args = make(0, n)
         t0 = time.perf_counter()
-        call(arrays)
+        call(args)
         return time.perf_counter() - t0
 
-    t_probe = run(8) / 8
-    n = int(min(S, max(8, budget_s / max(t_probe, 1e-9))))
+    n = min(units, 8)
     secs = run(n)
-    per_row = w.algorithmic_bytes() / S  # all rows valid in the timed workloads
-
-    # the same code on all host threads: disjoint row chunks, one call each
-    n_par = int(min(S, max(threads, threads * budget_s / (secs / n))))
+    while n < units and secs < 0.25:
+        n = min(units, n * 8)
+        secs = run(n)
+    reps = 1
+    if n < units and secs < budget_s:
+        n = int(min(units, max(n, n * budget_s / max(secs, 1e-9))))
+        secs = run(n)
+    elif n == units and secs < budget_s / 2:
+        args, reps = make(0, n), 0
+        t0 = time.perf_counter()
+        while reps < 1000 and time.perf_counter() - t0 < budget_s:
+            call(args)
+            reps += 1
+        secs = (time.perf_counter() - t0) / reps
+    n_par = int(min(units, max(threads, threads * budget_s / max(secs / n, 1e-12))))
     bounds = np.linspace(0, n_par, threads + 1).astype(int)
-    chunks = [sample(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
-    workers = [threading.Thread(target=call, args=(c,)) for c in chunks]
+    chunks = [make(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+
+    def work(c):
+        for _ in range(reps):
+            call(c)
+
+    workers = [threading.Thread(target=work, args=(c,)) for c in chunks]
     t0 = time.perf_counter()
     for t_ in workers:
         t_.start()
     for t_ in workers:
         t_.join()
-    par_secs = time.perf_counter() - t0
-    model = ""
+    return n, secs, reps, n_par, (time.perf_counter() - t0) / reps, len(workers)
+
+
+def _host_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
-        pass
+        return ""
+
+
+def cpu_baseline(path: str, w, x, budget_s: float, threads: int, *, nbytes=None, fp8_gemm=False):
+    """The C oracle on a bounded sample of the same workload, in the unit of
+    the path's metric: single-threaded, then the same code on disjoint chunks
+    in `threads` threads.  The layout and GEMM oracles compute every rank's
+    result of their call; their bytes (flops) count what they computed."""
+    import oracle  # CPU checker; only this leg of the benchmark uses it
+
+    S, r, tp = w.shard_rows, w.rank, w.tp
+    scale, unit, extra = 1e9, "GB/s", {}
+    if path == "fused":
+        roff = r * S if w.residual_replicated else 0
+        out_dt = (oracle.ORC_E2M1 if w.fp4 else oracle.ORC_BF16 if w.out_dtype == torch.bfloat16
+                  else oracle.ORC_E4M3)
+        sscale = static_scale() if w.quant_mode == QUANT_STATIC_TENSOR else 1.0
+        wt = _host_bits(x["weight"])
+        bias = None if x["bias"] is None else _host_bits(x["bias"])
+
+        def make(a, b):  # rows [a, b) of the shard as a compact shard of their own (all valid)
+            D = None if x["deepstack"] is None else _host_bits(x["deepstack"][r * S + a:r * S + b])
+            return (_host_bits(x["partials"][:, a:b]), _host_bits(x["residual"][roff + a:roff + b]), D)
+
+        def call(arr):
+            P, R, D = arr
+            oracle.reduce_add_rmsnorm(P, R, wt, bias, w.eps, w.quant_mode, D, tp_rank=r,
+                                      num_tokens=tp * P.shape[1], out_dtype=out_dt,
+                                      static_scale=sscale, want_debug=False)
+
+        units, per_unit, what = S, w.algorithmic_bytes() / S, f"rows of the rank-{r} shard ({w.name})"
+    elif path == "gather":
+        shards, scales = x[0], x[1]
+
+        def make(a, b):
+            return ([_host_bits(t[a:b]) for t in shards],
+                    None if scales is None else [_host_bits(t[a:b]) for t in scales])
+
+        def call(arr):
+            oracle.all_gather_unpad(arr[0], arr[1], num_tokens=tp * arr[0][0].shape[0])
+
+        units, per_unit = S, tp * nbytes / w.num_tokens
+        what = f"rows of each of the {tp} shards, gathered ({w.name})"
+    elif path == "fc2":
+        srcs = x[0]
+        G = len(srcs)
+
+        def make(a, b):  # tokens [G*a, G*b) of every source
+            return [_host_bits(t[G * a:G * b]) for t in srcs]
+
+        def call(arr):
+            oracle.fc2_regroup(arr, FC2_OTP)
+
+        units = w.num_tokens_pad // G
+        per_unit = G * nbytes / units  # every destination of the group
+        what = f"token groups of {G} (all {G} destinations of the group, {w.name})"
+    elif path == "dsacp":
+        attn = x[0]
+
+        def make(a, b):
+            return [_host_bits(t[a:b]) for t in attn]
+
+        def call(arr):
+            oracle.dsacp_heads_to_tokens(arr)
+
+        units, per_unit = S, tp * nbytes / S  # every rank's destination
+        what = f"rows of each rank's tokens (all {tp} destinations, {w.name})"
+    elif path == "gemm":
+        scale, unit = 1e12, "TFLOP/s"
+        if fp8_gemm:
+            x8, xs, w8, ws = x[0], x[1], x[2], x[3]
+            wh, wsh = _host_bits(w8), _host_bits(ws)
+
+            def make(a, b):
+                return _host_bits(x8[a:b]), _host_bits(xs[a:b] if xs.numel() > 1 else xs)
+
+            def call(arr):
+                oracle.scaled_matmul_scatter(arr[0], arr[1], wh, wsh, tp=1, rank=0,
+                                             out_dtype=oracle.ORC_BF16)
+        else:
+            xb, wb = x[0], x[1]
+            wh = _host_bits(wb)
+
+            def make(a, b):
+                return _host_bits(xb[a:b])
+
+            def call(arr):
+                oracle.matmul_scatter(arr, wh, tp=1, rank=0, out_dtype=oracle.ORC_BF16)
+
+        units = x[0].shape[0]
+        per_unit = nbytes / units  # flops per token row
+        what = f"token rows of x against the whole weight, one destination ({w.name})"
+    else:
+        raise ValueError(path)
+
+    n, secs, reps, n_par, par_secs, nthr = _oracle_legs(units, make, call, budget_s, threads)
+    rep = f" per call, mean of {reps} calls" if reps > 1 else ""
+    if path == "fused":
+        extra = {"tokens_per_s": round(n / secs, 2)}
     return {
-        "value": round(n * per_row / secs / 1e9, 4),
-        "unit": "GB/s",
+        "value": float(f"{n * per_unit / secs / scale:.4g}"),
+        "unit": unit,
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {n} of {S} rows of the rank-{r} shard ({w.name}); {secs:.1f} s; "
-                  f"{n / secs:.1f} shard tokens/s",
-        "tokens_per_s": round(n / secs, 2),
-        "seconds": round(secs, 2),
-        "parallel": {"value": round(n_par * per_row / par_secs / 1e9, 4), "unit": "GB/s",
-                     "cores": len(workers), "tokens_per_s": round(n_par / par_secs, 2),
-                     "seconds": round(par_secs, 2),
-                     "sample": f"first {n_par} of {S} rows in {len(workers)} disjoint chunks, "
-                               f"one thread each"},
-        "host": {"cpu": model, "logical_cpus": os.cpu_count()},
+        "sample": f"first {n} of {units} {what}; {secs:.3g} s{rep}"
+                  + (f"; {n / secs:.1f} shard tokens/s" if path == "fused" else ""),
+        **extra,
+        "seconds": float(f"{secs:.4g}"),
+        **({"repeats": reps} if reps > 1 else {}),
+        "parallel": {"value": float(f"{n_par * per_unit / par_secs / scale:.4g}"), "unit": unit,
+                     "cores": nthr, "seconds": float(f"{par_secs:.4g}"),
+                     **({"tokens_per_s": round(n_par / par_secs, 2)} if path == "fused" else {}),
+                     "sample": f"first {n_par} of {units} in {nthr} disjoint chunks, one thread each{rep}"},
+        "host": {"cpu": _host_model(), "logical_cpus": os.cpu_count()},
     }
 
 
@@ -579,8 +677,9 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if args.cpu_budget > 0 and args.path == "fused":
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget, max(1, args.cpu_threads))
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(args.path, w, x, args.cpu_budget, max(1, args.cpu_threads),
+                                              nbytes=nbytes, fp8_gemm=fp8_gemm)
     if gemm and fp8_gemm:
         result["context"] = {"hipblaslt_scaled_mm_us": library_fp8_gemm_us(x[0], x[1], x[2], x[3]),
                              "note": "torch._scaled_mm (hipBLASLt) on the same codes and scales, "
