@@ -64,3 +64,32 @@ def test_gemm_leg_counts_flops(fp8):
     cb = bench.cpu_baseline("gemm", w, x, BUDGET, 2, nbytes=2 * M * K * N, fp8_gemm=fp8)
     _check(cb, "TFLOP/s")
     assert f"of {M} token rows" in cb["sample"]
+
+
+# ---- command line: refusals that come before any device is touched
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench(*args, env=None):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=120,
+                          env={**os.environ, **(env or {})})
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+    r = _bench(env={"WORLD_SIZE": "4"})
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("args", [["--quant", "fp8"], ["--path", "gemm", "--quant", "mxfp8"],
+                                  ["--path", "gather", "--quant", "mxfp4"]])
+def test_inconsistent_options_are_refused(args):
+    r = _bench(*args)
+    assert r.returncode == 2 and "error" in r.stderr and r.stdout == ""
