@@ -37,6 +37,9 @@ SP_FLAG_VALID_ROWS_ONLY = 1
 
 
 class SprmsError(RuntimeError):
+    """A libsprms call returned a non-zero sp_status; `status` holds it and the
+    message the library's detail (sp_last_error) for that call."""
+
     def __init__(self, status: int, message: str):
         super().__init__(f"[{status}] {message}")
         self.status = status
@@ -529,8 +532,10 @@ def sp_shard_geometry(num_tokens: int, num_tokens_pad: int, tp: int, rank: int):
 
 
 def sp_error_string(status: int) -> str:
+    """The library's fixed name of an sp_status code."""
     return load().sp_error_string(int(status)).decode()
 
 
 def sp_last_error() -> str:
+    """Detail of the last failed call on this host thread (empty if none failed)."""
     return load().sp_last_error().decode()
