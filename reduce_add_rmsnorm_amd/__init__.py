@@ -537,5 +537,5 @@ def sp_error_string(status: int) -> str:
 
 
 def sp_last_error() -> str:
-    """Detail of the last failed call on this host thread (empty if none failed)."""
+    """Detail of the last failed call on this host thread ("no error" if none has failed)."""
     return load().sp_last_error().decode()
