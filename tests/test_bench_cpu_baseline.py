@@ -93,3 +93,24 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_inconsistent_options_are_refused(args):
     r = _bench(*args)
     assert r.returncode == 2 and "error" in r.stderr and r.stdout == ""
+
+
+# ---- roofline.traffic: counter bytes only while the kernel source is the one they were taken on
+
+def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
+    rec = {"C5": {"kernel": "sprms_kernel", "kernel_sha256_16": bench.kernel_hash("fused"),
+                  "hbm_bytes_per_launch": 123456789},
+           "C4": {"kernel": "sprms_kernel", "kernel_sha256_16": "0" * 16, "hbm_bytes_per_launch": 1},
+           "C5-gemm-None": {"kernel": "matmul_scatter_kernel", "kernel_sha256_16": bench.kernel_hash("gemm"),
+                            "hbm_bytes_per_launch": 42}}
+    f = tmp_path / "pmc_traffic.md"
+    f.write_text("# counters\n\n<!-- traffic " + __import__("json").dumps(rec) + " -->\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("C5") == 123456789
+    assert bench.measured_traffic("C4") is None                 # taken on another source
+    assert bench.measured_traffic("C3") is None                 # never measured
+    assert bench.measured_traffic("C5-gemm-None", "gemm") == 42
+    assert bench.measured_traffic("C5-gemm-None", "fused") is None  # hash of the wrong kernel
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic("C5") is None
+
