@@ -262,14 +262,15 @@ def all_gather_unpad(shards, scales=None, *, num_tokens):
     shards = [np.ascontiguousarray(a) for a in shards]
     tp = len(shards)
     S = shards[0].shape[0]
-    row_bytes = shards[0].nbytes // max(S, 1)
+    # row widths from the shapes, so that empty shards (S = 0) keep them
+    row_bytes = int(np.prod(shards[0].shape[1:], dtype=np.int64)) * shards[0].dtype.itemsize
     out = np.zeros((num_tokens,) + shards[0].shape[1:], dtype=shards[0].dtype)
     src = (C.c_void_p * tp)(*[a.ctypes.data for a in shards])
     ssrc, out_scale, srow = None, None, 0
     if scales is not None:
         scales = [np.ascontiguousarray(a) for a in scales]
         ssrc = (C.c_void_p * tp)(*[a.ctypes.data for a in scales])
-        srow = scales[0].nbytes // max(S, 1)
+        srow = int(np.prod(scales[0].shape[1:], dtype=np.int64)) * scales[0].dtype.itemsize
         out_scale = np.zeros((num_tokens,) + scales[0].shape[1:], dtype=scales[0].dtype)
     rc = lib.orc_all_gather_unpad(tp, S, row_bytes, num_tokens, src, srow, ssrc, _ptr(out),
                                   _ptr(out_scale))

@@ -465,6 +465,16 @@ def test_all_gather_unpad_worked_example():
     assert T - start == valid and S - valid == g["pad_rows_total"]
 
 
+def test_all_gather_unpad_of_empty_shards():
+    # S = 0 (no tokens in the step): nothing to gather, as the library allows
+    for scaled in (False, True):
+        shards = [np.empty((0, 16), np.uint8) for _ in range(3)]
+        scales = [np.empty((0,), np.float32) for _ in range(3)] if scaled else None
+        out, out_scale = oracle.all_gather_unpad(shards, scales, num_tokens=0)
+        assert out.shape == (0, 16) and (out_scale is None) == (not scaled)
+        assert not scaled or out_scale.shape == (0,)
+
+
 
 # ------------------------------------------------ block scaling (MX form)
 
