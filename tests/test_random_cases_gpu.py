@@ -16,7 +16,7 @@ from parity import run_case
 from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK, QUANT_NONE,
                                            QUANT_STATIC_TENSOR, WORKLOADS)
 
-N_CASES = 48
+N_CASES = 64
 
 
 @pytest.fixture(scope="module")

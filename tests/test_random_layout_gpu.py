@@ -15,7 +15,7 @@ from helpers import to_host
 from test_matmul_gpu import (_check, _check_fp8, _e4m3_codes, _operands, _receive_buffers,
                              _slots_untouched)
 
-N_CASES = 16
+N_CASES = 32
 CANARY = 0xA5
 
 
