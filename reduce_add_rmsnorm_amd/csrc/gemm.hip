@@ -22,18 +22,19 @@
 //   * the weight tile is the MFMA's A operand and the token tile its B
 //     operand, so each lane's accumulators are 4-element runs of one token
 //     row's output columns;
-//   * K advances 64 at a time through two LDS stages filled by buffer loads
-//     that write LDS directly (16 bytes per lane, no staging registers).
-//     bf16 is software-pipelined: a stage's fragments are all in registers
-//     when its step begins, each is refilled from the next stage right after
-//     its last MFMA, and the loads two stages ahead are spread over the
-//     first k-step (~8% faster than reading each k-step's fragments at its
-//     start, which left every wavefront waiting on LDS at each barrier).
-//     e4m3 issues the next stage's loads before the current stage's MFMAs
-//     and reads fragments per k-step (the pipelined form was slower there).
-//     LDS rows are 128 bytes with
-//     their 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 rows an
-//     MFMA operand read touches per 16 lanes land on distinct banks;
+//   * K advances 128 bytes of each row at a time (64 bf16 or 128 e4m3
+//     elements) through two LDS stages filled by buffer loads that write LDS
+//     directly (16 bytes per lane, no staging registers).  bf16 is
+//     software-pipelined: a stage's fragments are all in registers when its
+//     step begins, each is refilled from the next stage right after its last
+//     MFMA, and the loads two stages ahead are spread over the first k-step
+//     (6-8% faster than reading each k-step's fragments at its start, which
+//     left every wavefront waiting on LDS at each barrier).  e4m3 issues the
+//     next stage's loads before the current stage's MFMAs and reads
+//     fragments per k-step (the pipelined form was slower there).  LDS rows
+//     are 128 bytes with their 16-byte chunks XOR-swizzled by (row >> 1) & 7,
+//     so the 16 rows an MFMA operand read touches per 16 lanes land on
+//     distinct banks;
 //   * the epilogue stages the rounded tile in LDS and writes each token row
 //     as 512 contiguous bytes (16 per lane): written from the accumulator
 //     layout directly, every 8-byte piece became its own DRAM write, 4x the
