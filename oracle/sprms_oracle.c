@@ -29,6 +29,14 @@
  * gain; deepstack added before the residual; the norm and quantiser use the
  * unrounded sum, not the stored residual; qmax = 448 (OCP e4m3fn);
  * an all-zero row in dynamic mode gets scale 0 and zero codes.
+ *
+ * NaN (the pages say nothing about it; inputs are normally finite): the
+ * arithmetic is IEEE, so a NaN input element makes z NaN there, the row's
+ * sum of squares and so every y of the row NaN; a NaN gain or bias element
+ * makes y NaN in that column.  Every NaN reaches the output: bf16/f32 NaN,
+ * the e4m3 NaN code 0x7F (never a saturated code), a NaN per-token scale
+ * (the row maximum skips nothing) with every code of the row 0x7F, and the
+ * E8M0 NaN byte 0xFF for a block holding a NaN.
  */
 #include "sprms_oracle.h"
 
@@ -320,12 +328,13 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
     for (int64_t h = 0; h < H; ++h) ss += z[h] * z[h];
     const double rstd = 1.0 / sqrt(ss / (double)H + (double)eps);
 
-    /* y = z * rstd * weight (+ bias) and its absolute maximum */
+    /* y = z * rstd * weight (+ bias) and its absolute maximum; a NaN
+     * anywhere in y makes the maximum NaN (nothing is skipped) */
     double amax = 0.0;
     for (int64_t h = 0; h < H; ++h) {
       y[h] = z[h] * rstd * load(weight, p->act_dtype, h);
       if (bias) y[h] += load(bias, p->act_dtype, h);
-      if (fabs(y[h]) > amax) amax = fabs(y[h]);
+      if (isnan(y[h]) || fabs(y[h]) > amax) amax = fabs(y[h]);
     }
 
     if (quant_mode == ORC_QUANT_NONE) {
@@ -334,22 +343,39 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
       /* codes encode y / scale, scale a calibrated per-tensor constant */
       for (int64_t h = 0; h < H; ++h) store(out, ORC_E4M3, i * H + h, y[h] / (double)static_scale);
     } else if (quant_mode == ORC_QUANT_DYNAMIC_TOKEN) {
-      /* per-token scale = max|y| / qmax, qmax = 448; codes encode y / scale */
+      /* per-token scale = max|y| / qmax, qmax = 448; codes encode y / scale.
+       * A zero row has scale 0 and zero codes; a row holding a NaN has a
+       * NaN scale, so every code of it is the NaN code. */
       const float scale = (float)(amax / 448.0);
       ((float*)out_scale)[i] = scale;
       for (int64_t h = 0; h < H; ++h)
-        store(out, ORC_E4M3, i * H + h, scale > 0.0f ? y[h] / (double)scale : 0.0);
+        store(out, ORC_E4M3, i * H + h, scale == 0.0f ? 0.0 : y[h] / (double)scale);
     } else {
       /* per-block scaling in the OCP microscaling form: for each block of 32
        * consecutive elements, X = 2^e with e = floor(log2(max|y|)) - emax
        * (emax = 8 for e4m3, 2 for e2m1; clamped to the E8M0 range [-127, 127];
        * an all-zero block takes -127), elements encode y / X with saturation,
-       * the scale is stored as the E8M0 byte e + 127. */
+       * the scale is stored as the E8M0 byte e + 127.  A block holding a NaN
+       * takes the E8M0 NaN byte 0xFF, which makes the whole block NaN in that
+       * format; its elements are then written as the e4m3 NaN code, or as 0
+       * in e2m1, which has no NaN code. */
       const int emax = p->out_dtype == ORC_E4M3 ? 8 : 2;
       for (int64_t b = 0; b < nblk; ++b) {
         double bmax = 0.0;
         for (int64_t h = 32 * b; h < 32 * b + 32; ++h)
-          if (fabs(y[h]) > bmax) bmax = fabs(y[h]);
+          if (isnan(y[h]) || fabs(y[h]) > bmax) bmax = fabs(y[h]);
+        if (isnan(bmax)) {
+          ((uint8_t*)out_scale)[i * nblk + b] = 0xFF;
+          for (int64_t h = 32 * b; h < 32 * b + 32; ++h) {
+            if (p->out_dtype == ORC_E4M3) {
+              ((uint8_t*)out)[i * H + h] = 0x7F;
+            } else {
+              uint8_t* byte = (uint8_t*)out + (size_t)i * orow + (size_t)(h / 2);
+              *byte = (h % 2 == 0) ? (uint8_t)(*byte & 0xF0) : (uint8_t)(*byte & 0x0F);
+            }
+          }
+          continue;
+        }
         int e = -127;
         if (bmax > 0.0) {
           int k;
@@ -392,6 +418,16 @@ void orc_e4m3_from_double_n(const double* x, int64_t n, uint8_t* out) {
 
 /* ------------------------------------------ the boundary's argument list */
 
+/* [a, a+an) and [b, b+bn) share a byte; empty ranges share nothing */
+static int spans_meet(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return 0;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+/* largest byte span the partials may cover: 2^47 bytes, beyond any device */
+#define ORC_MAX_SPAN ((int64_t)1 << 47)
+
 int sp_oracle_reduce_add_rmsnorm(const orc_abi_problem* a, const void* partials, void* residual,
                                  const void* weight, const void* bias, float eps, int quant_mode,
                                  const void* deepstack, void* out, void* out_scale, void* stream) {
@@ -417,6 +453,44 @@ int sp_oracle_reduce_add_rmsnorm(const orc_abi_problem* a, const void* partials,
   if (!pe || !az || !orow) return ORC_ERR_DTYPE;
   const int64_t stride = a->partial_stride ? a->partial_stride : S * H;
   if (stride < S * H) return ORC_ERR_SHAPE;
+  /* bytes from the first partial row to the end of the last: (tp-1)*stride
+   * + S*H elements, which must neither overflow nor pass ORC_MAX_SPAN */
+  int64_t span_elems, span_bytes;
+  if (__builtin_mul_overflow(tp - 1, stride, &span_elems) ||
+      __builtin_add_overflow(span_elems, S * H, &span_elems) ||
+      __builtin_mul_overflow(span_elems, (int64_t)pe, &span_bytes) || span_bytes > ORC_MAX_SPAN)
+    return ORC_ERR_SHAPE;
+
+  /* The rows this call writes may share no byte with what it reads, nor
+   * with each other: the residual rows updated in place (residual_out NULL,
+   * or pointing at the block in use) only with the residual itself. */
+  int64_t v = a->num_tokens - (int64_t)a->tp_rank * S;
+  v = v < 0 ? 0 : (v > S ? S : v);
+  const int64_t n = (a->flags & 1) ? v : S;  /* rows written */
+  const int64_t roff = (a->residual_rows == tp * S && tp > 1) ? (int64_t)a->tp_rank * S : 0;
+  const char* used = (const char*)residual + (size_t)(roff * H) * az;
+  void* res_dst = a->residual_out ? a->residual_out : (void*)used;
+  {
+    const int in_place = res_dst == (const void*)used;
+    const size_t row_az = (size_t)H * az;
+    /* inputs; the static scale (one f32) is read, the other scales written */
+    const void* in_p[6] = {partials, weight, bias, deepstack, residual, out_scale};
+    const size_t in_n[6] = {(size_t)span_bytes, row_az, bias ? row_az : 0,
+                            deepstack ? (size_t)a->deepstack_rows * row_az : 0,
+                            (size_t)a->residual_rows * row_az,
+                            quant_mode == ORC_QUANT_STATIC_TENSOR ? 4 : 0};
+    const void* out_p[3] = {res_dst, out, out_scale};
+    const size_t out_n[3] = {(size_t)n * row_az, (size_t)n * orow,
+                             dyn ? (size_t)n * 4 : blk ? (size_t)n * (size_t)(H / 32) : 0};
+    for (int o = 0; o < 3; ++o) {
+      for (int k = 0; k < 6; ++k) {
+        if (o == 0 && k == 4 && in_place) continue; /* the in-place update itself */
+        if (spans_meet(out_p[o], out_n[o], in_p[k], in_n[k])) return ORC_ERR_SHAPE;
+      }
+      for (int o2 = o + 1; o2 < 3; ++o2)
+        if (spans_meet(out_p[o], out_n[o], out_p[o2], out_n[o2])) return ORC_ERR_SHAPE;
+    }
+  }
 
   /* a strided set of partials is packed into [tp][S][H] first */
   void* packed = NULL;
@@ -437,11 +511,6 @@ int sp_oracle_reduce_add_rmsnorm(const orc_abi_problem* a, const void* partials,
                                 quant_mode, deepstack, static_scale, S, NULL, res_t, out_t,
                                 (dyn || blk) ? sc_t : NULL, NULL, NULL);
   if (rc == ORC_OK) {
-    int64_t v = a->num_tokens - (int64_t)a->tp_rank * S;
-    v = v < 0 ? 0 : (v > S ? S : v);
-    const int64_t n = (a->flags & 1) ? v : S;  /* rows written */
-    const int64_t roff = (a->residual_rows == tp * S && tp > 1) ? (int64_t)a->tp_rank * S : 0;
-    void* res_dst = a->residual_out ? a->residual_out : (char*)residual + (size_t)(roff * H) * az;
     memcpy(res_dst, res_t, (size_t)(n * H) * az);
     memcpy(out, out_t, (size_t)n * orow);
     if (dyn || blk) memcpy(out_scale, sc_t, (size_t)n * srow);

@@ -104,6 +104,12 @@ int orc_reduce_add_rmsnorm(const orc_problem* p, const void* partials,
  *   partial_scale          0 is read as 1;
  *   out_scale              static: [1] read; dynamic: [S] f32 written; block:
  *                          [S][H/32] E8M0 bytes written.
+ * Rejected with ORC_ERR_SHAPE before anything is read or written: partials
+ * whose byte span, (tp-1)*stride + S*H elements, overflows or exceeds 2^47
+ * bytes; a written byte (residual rows, out, out_scale) that the call also
+ * reads (partials, gain, bias, deepstack, residual, the static scale) or
+ * writes twice -- the one exception being the residual rows in use updated
+ * in place (residual_out NULL or equal to them).
  * Every output is computed before the first write, so a call that returns
  * an error has written nothing. */
 typedef struct {

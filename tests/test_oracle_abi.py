@@ -214,3 +214,64 @@ def test_errors_write_nothing():
     assert oracle.sp_oracle_reduce_add_rmsnorm(p, *args, QUANT_DYNAMIC_TOKEN, h["deepstack"], out, None) \
         == oracle_err("NULL")
     assert (out == 0xA5).all() and (res == 0xA5A5).all() and np.isnan(sc).all()
+
+
+def test_in_place_residual_may_not_share_bytes_with_what_the_call_reads():
+    # [PR18671] §5.2 raises on a layout mismatch rather than corrupting shared
+    # storage; here the residual rows updated in place (residual_out NULL, or
+    # the block in use) must not overlap the partials, gain, bias or deepstack.
+    w = _small("C5")
+    h = _host_inputs(w, 3)
+    tp, S, H = h["partials"].shape
+    _, out, sc = _outputs(h, oracle.ORC_E4M3, QUANT_DYNAMIC_TOKEN)
+    buf = h["partials"].copy()
+    inside = buf[1]  # partial 1's rows, used as this shard's residual
+    before = buf.copy()
+    for res_out in (None, inside.ctypes.data):
+        p = _problem(h, w, 3, oracle.ORC_E4M3, residual_rows=S, residual_out=res_out)
+        rc = oracle.sp_oracle_reduce_add_rmsnorm(p, buf, inside, h["weight"], None, w.eps,
+                                                 QUANT_DYNAMIC_TOKEN, h["deepstack"], out, sc)
+        assert rc == oracle_err("SHAPE")
+    np.testing.assert_array_equal(buf, before)
+    # the gain, the bias or the deepstack inside the residual block
+    res = h["residual"][-S:].copy()
+    for k in ("weight", "bias", "deepstack"):
+        args = {"weight": h["weight"], "bias": None, "deepstack": h["deepstack"]}
+        args[k] = res[2] if k != "deepstack" else res
+        p = _problem(h, w, 3, oracle.ORC_E4M3, residual_rows=S,
+                     deepstack_rows=0 if args["deepstack"] is None else args["deepstack"].shape[0])
+        rc = oracle.sp_oracle_reduce_add_rmsnorm(p, h["partials"], res, args["weight"], args["bias"],
+                                                 w.eps, QUANT_DYNAMIC_TOKEN, args["deepstack"], out, sc)
+        assert rc == oracle_err("SHAPE"), k
+    # the same residual, on its own, updated in place is fine
+    p = _problem(h, w, 3, oracle.ORC_E4M3)
+    assert oracle.sp_oracle_reduce_add_rmsnorm(p, h["partials"], h["residual"].copy(), h["weight"],
+                                               None, w.eps, QUANT_DYNAMIC_TOKEN, h["deepstack"],
+                                               out, sc) == 0
+
+
+def test_static_scale_may_not_share_bytes_with_an_output():
+    w = _small("C4")
+    h = _host_inputs(w, 7)
+    res, out, _ = _outputs(h, oracle.ORC_E4M3, QUANT_STATIC_TENSOR)
+    p = _problem(h, w, 7, oracle.ORC_E4M3)
+    p.residual_out = res.ctypes.data
+    sc = out.reshape(-1)[:4].view(np.float32)
+    sc[0] = 0.02
+    assert oracle.sp_oracle_reduce_add_rmsnorm(p, h["partials"], h["residual"], h["weight"], None, w.eps,
+                                               QUANT_STATIC_TENSOR, None, out, sc) == oracle_err("SHAPE")
+
+
+@pytest.mark.parametrize("stride", [2 ** 62, 2 ** 63 - 64, 2 ** 46])
+def test_partial_stride_that_overflows_or_spans_too_far_is_rejected(stride):
+    # (tp - 1) * stride + S*H elements must be a byte span of at most 2^47;
+    # nothing is read when it is not
+    w = _small("C4")
+    h = _host_inputs(w, 7)
+    res, out, _ = _outputs(h, oracle.ORC_E4M3, QUANT_STATIC_TENSOR)
+    p = _problem(h, w, 7, oracle.ORC_E4M3, partial_stride=stride)
+    p.residual_out = res.ctypes.data
+    sc = np.array([0.02], np.float32)
+    assert oracle.sp_oracle_reduce_add_rmsnorm(p, h["partials"], h["residual"], h["weight"], None, w.eps,
+                                               QUANT_STATIC_TENSOR, None, out, sc) == oracle_err("SHAPE")
+    assert (out == 0xA5).all()

@@ -69,6 +69,13 @@ MUTATIONS = {
                              "const double sw = (double)w_scale[w_scale_rows == 1 ? 0 : m % N];"),
     "gather_rows_reversed": ("(const char*)shards[q] + (size_t)(s * row_bytes),",
                              "(const char*)shards[q] + (size_t)((S - 1 - s) * row_bytes),"),
+    "row_max_skips_nan": ("if (isnan(y[h]) || fabs(y[h]) > amax) amax = fabs(y[h]);",
+                          "if (fabs(y[h]) > amax) amax = fabs(y[h]);"),
+    "nan_scale_gives_zero_codes": ("scale == 0.0f ? 0.0 : y[h] / (double)scale",
+                                   "scale > 0.0f ? y[h] / (double)scale : 0.0"),
+    "block_max_skips_nan": ("if (isnan(y[h]) || fabs(y[h]) > bmax) bmax = fabs(y[h]);",
+                            "if (fabs(y[h]) > bmax) bmax = fabs(y[h]);"),
+    "nan_saturates_to_448": ("if (isnan(x)) return 0x7F;", "if (isnan(x)) return 0x7E;"),
     "gather_scale_from_wrong_rank": ("(const char*)scales[q] + (size_t)(s * scale_row_bytes)",
                                      "(const char*)scales[0] + (size_t)(s * scale_row_bytes)"),
 }
@@ -82,6 +89,10 @@ ABI_MUTATIONS = {
     "abi_valid_rows_flag_ignored": ("const int64_t n = (a->flags & 1) ? v : S;", "const int64_t n = S;"),
     "abi_stride_ignored": ("if (partials && stride != S * H) {", "if (0) {"),
     "abi_static_scale_not_read": ("static_scale = ((const float*)out_scale)[0];", "static_scale = 1.0f;"),
+    "abi_in_place_overlap_allowed": ("if (o == 0 && k == 4 && in_place) continue;",
+                                     "if (o == 0 && in_place) continue;"),
+    "abi_static_scale_not_an_input": ("quant_mode == ORC_QUANT_STATIC_TENSOR ? 4 : 0};", "0};"),
+    "abi_span_unbounded": ("span_bytes > ORC_MAX_SPAN)", "span_bytes < 0)"),
     "abi_zero_partial_scale_kept": ("a->partial_scale == 0.0f ? 1.0 :", "a->partial_scale == 0.0f ? 0.0 :"),
 }
 

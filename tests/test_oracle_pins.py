@@ -400,6 +400,116 @@ def test_partial_shard_padding():
     assert not np.any(out["out"][1:]) and not np.any(out["residual_out"][1:])
 
 
+# ------------------------------------------------------------------- NaN
+#
+# The pages say nothing about NaN.  The reading taken: IEEE arithmetic all
+# the way, and every NaN reaches the output in the format's own NaN
+# encoding -- the OCP e4m3 NaN code S.1111.111 (never a saturated code), the
+# E8M0 NaN byte 0xFF of the OCP microscaling format (which makes its whole
+# block NaN), IEEE NaN for bf16/f32 and for the per-token scale.  What pins
+# it beyond those definitions: a NaN cannot change any output it does not
+# feed (rows and, for a gain or bias NaN, columns and blocks elsewhere stay
+# bit-identical to a run without it), and one NaN in z reaches every y of its
+# row through the sum of squares.
+
+_NAN_MODES = [(NONE, oracle.ORC_BF16), (NONE, oracle.ORC_F32), (STATIC, oracle.ORC_E4M3),
+              (DYNAMIC, oracle.ORC_E4M3), (MX, oracle.ORC_E4M3), (MX, oracle.ORC_E2M1)]
+
+
+def _nan_setup(seed=11, tp=2, S=3, H=64):
+    rng = np.random.default_rng(seed)
+    P = f32(rng.normal(0, 0.5, (tp, S, H)))
+    R = f32(rng.normal(0, 1, (S, H)))
+    w = f32(rng.normal(1, 0.1, H))
+    b = f32(rng.normal(0, 0.02, H))
+    return P, R, w, b
+
+
+def _is_nan_out(out, od):
+    if od == oracle.ORC_BF16:
+        return np.isnan(bf16_bits_to_f64(out))
+    if od == oracle.ORC_F32:
+        return np.isnan(out)
+    return None
+
+
+def _assert_all_nan(res, row, od, quant):
+    """Every output of shard row `row` is NaN in its format's encoding."""
+    out = res["out"][row]
+    if quant == NONE:
+        assert _is_nan_out(out, od).all()
+    elif quant in (STATIC, DYNAMIC) or (quant == MX and od == oracle.ORC_E4M3):
+        assert (out == 0x7F).all()
+    else:  # MX e2m1: no NaN code, the 0xFF scale carries it
+        assert not out.any()
+    if quant == DYNAMIC:
+        assert np.isnan(res["out_scale"][row])
+    if quant == MX:
+        assert (res["out_scale"][row] == 0xFF).all()
+
+
+@pytest.mark.parametrize("quant,od", _NAN_MODES)
+@pytest.mark.parametrize("where", ["partial", "residual", "deepstack"])
+def test_nan_input_in_a_valid_row_reaches_every_output_of_that_row(quant, od, where):
+    P, R, w, b = _nan_setup()
+    D = f32(np.random.default_rng(3).normal(0, 0.3, R.shape))
+    clean = _run(P, R, w, b, eps=1e-6, quant=quant, deepstack=D, out_dtype=od, static_scale=0.01)
+    P2, R2, D2 = P.copy(), R.copy(), D.copy()
+    {"partial": P2[1], "residual": R2, "deepstack": D2}[where][1, 5] = np.nan
+    got = _run(P2, R2, w, b, eps=1e-6, quant=quant, deepstack=D2, out_dtype=od, static_scale=0.01)
+    # the updated residual is NaN at that element only
+    nan_res = np.isnan(got["residual_out"])
+    assert nan_res[1, 5] and nan_res.sum() == 1
+    keep = np.ones(R.shape, bool)
+    keep[1, 5] = False
+    np.testing.assert_array_equal(got["residual_out"][keep], clean["residual_out"][keep])
+    # the row's sum of squares is NaN, so every y and every output of the row is
+    assert np.isnan(got["y"][1]).all()
+    _assert_all_nan(got, 1, od, quant)
+    # the other rows are untouched by it
+    for key in ("out", "out_scale", "residual_out"):
+        if key in got:
+            for r in (0, 2):
+                np.testing.assert_array_equal(got[key][r], clean[key][r])
+
+
+@pytest.mark.parametrize("quant,od", _NAN_MODES)
+@pytest.mark.parametrize("which", ["weight", "bias"])
+def test_nan_gain_or_bias_element_reaches_its_column(quant, od, which):
+    P, R, w, b = _nan_setup(seed=12)
+    h0 = 37  # inside block 1 (elements 32..63)
+    clean = _run(P, R, w, b, eps=1e-6, quant=quant, out_dtype=od, static_scale=0.01)
+    w2, b2 = w.copy(), b.copy()
+    (w2 if which == "weight" else b2)[h0] = np.nan
+    got = _run(P, R, w2, b2, eps=1e-6, quant=quant, out_dtype=od, static_scale=0.01)
+    # the residual and rstd do not involve the gain or bias
+    np.testing.assert_array_equal(got["residual_out"], clean["residual_out"])
+    assert np.isnan(got["y"][:, h0]).all()
+    others = np.ones(R.shape[1], bool)
+    others[h0] = False
+    np.testing.assert_array_equal(got["y"][:, others], clean["y"][:, others])
+    if quant == NONE:
+        assert _is_nan_out(got["out"][:, h0], od).all()
+        np.testing.assert_array_equal(got["out"][:, others], clean["out"][:, others])
+    elif quant == STATIC:
+        assert (got["out"][:, h0] == 0x7F).all()
+        np.testing.assert_array_equal(got["out"][:, others], clean["out"][:, others])
+    elif quant == DYNAMIC:
+        # the row maximum skips nothing: every row's scale is NaN
+        for r in range(R.shape[0]):
+            _assert_all_nan(got, r, od, quant)
+    else:
+        # only the block holding h0 is NaN; block 0 is as before
+        assert (got["out_scale"][:, 1] == 0xFF).all()
+        np.testing.assert_array_equal(got["out_scale"][:, 0], clean["out_scale"][:, 0])
+        if od == oracle.ORC_E4M3:
+            assert (got["out"][:, 32:64] == 0x7F).all()
+            np.testing.assert_array_equal(got["out"][:, :32], clean["out"][:, :32])
+        else:
+            assert not got["out"][:, 16:32].any()
+            np.testing.assert_array_equal(got["out"][:, :16], clean["out"][:, :16])
+
+
 # ---------------------------------------------------------------- validation
 
 
