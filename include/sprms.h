@@ -151,15 +151,27 @@ typedef struct {
  *
  * Arithmetic: fp32 throughout; partial sums in ascending rank order, then
  * deepstack, then residual; the norm and the quantiser use the unrounded fp32
- * sum; stores round to nearest even; e4m3 values are clamped to +-448.
+ * sum; stores round to nearest even; e4m3 numbers are clamped to +-448.
  * A dynamic row whose max |y| is 0 gets scale 0 and zero codes.
+ * NaN (the pages do not cover it) propagates and is never turned into a
+ * number: a NaN input element makes that residual_out element and every
+ * output of its row NaN (through the sum of squares); a NaN gain or bias
+ * element makes its column NaN.  NaN outputs are IEEE NaN in bf16/f32, the
+ * code 0x7F in e4m3; a per-token row holding a NaN gets scale NaN
+ * (0x7FC00000) and all codes 0x7F; a block holding a NaN gets the E8M0 NaN
+ * byte 0xFF and element codes 0x7F (e4m3) or 0 (e2m1).
  *
- * Ownership and errors: the caller owns every buffer; out and residual_out
- * must not overlap any input (residual_out may be NULL for in-place).  Every
- * check runs on the host before anything is enqueued, so a call that
- * returns an error has written nothing.  Returns SP_OK or a negative
- * sp_status; sp_last_error() gives the detail.  S == 0 enqueues nothing.
- * Rows outside [0, S) of out / residual_out are never touched.
+ * Ownership and errors: the caller owns every buffer.  No byte the call
+ * writes (residual_out or the residual rows updated in place, out,
+ * out_scale) may be read by it (partials, weight, bias, deepstack, the
+ * residual, the static scale) or written twice; the one exception is the
+ * in-place update (residual_out NULL, or equal to the residual rows in
+ * use).  The partials may span at most 2^47 bytes ((tp-1)*partial_stride +
+ * S*H elements).  Every check runs on the host before anything is enqueued,
+ * so a call that returns an error (SP_ERR_SHAPE for the rules above) has
+ * written nothing.  Returns SP_OK or a negative sp_status; sp_last_error()
+ * gives the detail.  S == 0 enqueues nothing.  Rows outside [0, S) of out /
+ * residual_out are never touched.
  */
 int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* residual,
                           const void* weight, const void* bias, float eps, int quant_mode,

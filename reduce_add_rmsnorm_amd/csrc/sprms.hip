@@ -30,7 +30,8 @@
 //     wavefronts through LDS with one barrier; with a bias the per-token max
 //     needs y, so a second LDS step follows;
 //   * output conversion uses gfx950's v_cvt_pk_bf16_f32 / v_cvt_pk_fp8_f32
-//     (OCP e4m3fn), after an explicit clamp to +-448; block scaling takes the
+//     (OCP e4m3fn), after an explicit clamp to +-448 that keeps NaN as NaN;
+//     maxima use v_maximum3_f32, which propagates NaN; block scaling takes the
 //     32-element max across a quad of lanes (DPP), an E8M0 exponent from
 //     v_frexp_exp, exact v_ldexp scaling and v_cvt_scalef32_pk_fp4_f32 for
 //     e2m1;
@@ -63,6 +64,9 @@ constexpr int max_threads() {
 
 enum OutMode { OM_BF16 = 0, OM_F32 = 1, OM_FP8_STATIC = 2, OM_FP8_DYN = 3, OM_MX_FP8 = 4, OM_MX_FP4 = 5 };
 constexpr int kMxBlock = 32;  // elements per block scale (4 lanes x 8 elements)
+// Largest byte span the partials may cover (beyond any device's memory); it
+// keeps every offset computed from the descriptor far from int64 overflow.
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 47;
 
 struct KArgs {
   const void* partials;   // [tp][S][H]
@@ -177,12 +181,23 @@ struct Vec<SP_F32> {
   }
 };
 
+// Largest of a and b, NaN if either is NaN (v_maximum3_f32); fmaxf would
+// return the number and drop the NaN.
+__device__ __forceinline__ float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Saturation to +-448 for numbers; a NaN becomes the positive quiet NaN, which
+// converts to the e4m3 NaN code 0x7F (fminf/fmaxf alone would turn it into
+// -448, a plausible-looking finite code).
+__device__ __forceinline__ float sat_e4m3(float t) {
+  return t == t ? fminf(fmaxf(t, -448.0f), 448.0f) : __builtin_nanf("");
+}
+
 // 8 fp32 -> 8 OCP e4m3fn codes (little-endian byte order = element order),
-// clamped to +-448 first so the conversion never sees an out-of-range value.
+// saturated first so the conversion never sees an out-of-range number.
 __device__ __forceinline__ u32x2 pack_e4m3(const float (&t)[kVec]) {
   float c[kVec];
 #pragma unroll
-  for (int k = 0; k < kVec; ++k) c[k] = fminf(fmaxf(t[k], -448.0f), 448.0f);
+  for (int k = 0; k < kVec; ++k) c[k] = sat_e4m3(t[k]);
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
@@ -239,18 +254,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
-// Max over the 4 lanes of a quad (lanes 4b..4b+3), in every lane of it.
+// Max over the 4 lanes of a quad (lanes 4b..4b+3), in every lane of it; NaN
+// if any of them holds NaN.
 __device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, dpp<kQuadSwap1>(v));
-  return fmaxf(v, dpp<kQuadSwap2>(v));
+  v = nan_max(v, dpp<kQuadSwap1>(v));
+  return nan_max(v, dpp<kQuadSwap2>(v));
 }
 
+// Max over the 64 lanes, NaN if any lane holds NaN.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<kQuadSwap1>(v));
-  v = fmaxf(v, dpp<kQuadSwap2>(v));
-  v = fmaxf(v, dpp<kRowRor4>(v));
-  v = fmaxf(v, dpp<kRowRor8>(v));
-  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+  v = nan_max(v, dpp<kQuadSwap1>(v));
+  v = nan_max(v, dpp<kQuadSwap2>(v));
+  v = nan_max(v, dpp<kRowRor4>(v));
+  v = nan_max(v, dpp<kRowRor8>(v));
+  return nan_max(nan_max(lane_read(v, 0), lane_read(v, 16)), nan_max(lane_read(v, 32), lane_read(v, 48)));
 }
 
 // ----------------------------------------------------------------- kernel
@@ -413,11 +430,11 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
     for (int k = 0; k < kVec; ++k) {
       part += z[i][k] * z[i][k];
       z[i][k] *= w[k];
-      m = fmaxf(m, fabsf(z[i][k]));
+      m = nan_max(m, fabsf(z[i][k]));
     }
     if (live[i]) {
       ss += part;
-      amax = fmaxf(amax, m);
+      amax = nan_max(amax, m);
     }
   }
 
@@ -434,7 +451,7 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
   amax = 0.0f;
   for (int w = 0; w < nw; ++w) {
     ss += red[0][w];
-    if constexpr (kFusedMax) amax = fmaxf(amax, red[1][w]);
+    if constexpr (kFusedMax) amax = nan_max(amax, red[1][w]);
   }
   const float rstd = 1.0f / sqrtf(ss / static_cast<float>(a.H) + a.eps);
 
@@ -461,20 +478,25 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
     for (int i = 0; i < VPT; ++i) {
       float m = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) m = fmaxf(m, fabsf(z[i][k]));
+      for (int k = 0; k < kVec; ++k) m = nan_max(m, fabsf(z[i][k]));
       m = quad_max(m);
+      // a block holding a NaN takes the E8M0 NaN byte 0xFF (the whole block
+      // reads as NaN); its elements become the e4m3 NaN code, or 0 in e2m1,
+      // which has no NaN code
+      const bool nan_block = m != m;
       // floor(log2 m) = frexp exponent - 1 (exact, subnormals included)
       int e = m > 0.0f ? __builtin_amdgcn_frexp_expf(m) - 1 - kEmax : -127;
       e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      constexpr float kNanElt = OM == OM_MX_FP8 ? __builtin_nanf("") : 0.0f;
       float t[kVec];
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) t[k] = __builtin_ldexpf(z[i][k], -e);
+      for (int k = 0; k < kVec; ++k) t[k] = nan_block ? kNanElt : __builtin_ldexpf(z[i][k], -e);
       if (live[i]) {
         if constexpr (OM == OM_MX_FP8) store_e4m3(r_out, vec[i] * 8, pack_e4m3(t));
         else store_e2m1(r_out, vec[i] * 4, pack_e2m1(t));
         if ((tid & 3) == 0)
-          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(e + 127), r_sc, vec[i] / 4, 0,
-                                               kStorePolicy);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(nan_block ? 0xFF : e + 127), r_sc,
+                                               vec[i] / 4, 0, kStorePolicy);
       }
     }
   } else {
@@ -483,7 +505,8 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
       inv = 1.0f / static_scale;
     } else {
       // max |y|: without bias, rounding is monotone so max|zw*rstd| equals
-      // max|zw| * rstd exactly; with bias it needs a pass over y.
+      // max|zw| * rstd exactly; with bias it needs a pass over y.  A NaN
+      // anywhere in the row makes it NaN (a NaN z makes rstd NaN).
       float ymax;
       if (!has_bias) {
         ymax = amax * rstd;
@@ -493,17 +516,21 @@ __device__ __forceinline__ void process_row(const KArgs& a, const int64_t s, flo
         for (int i = 0; i < VPT; ++i)
           if (live[i]) {
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) m = fmaxf(m, fabsf(z[i][k]));
+            for (int k = 0; k < kVec; ++k) m = nan_max(m, fabsf(z[i][k]));
           }
         m = wave_max(m);
         if (lane == 0) red[2][wave] = m;
         __syncthreads();
         ymax = 0.0f;
-        for (int w = 0; w < nw; ++w) ymax = fmaxf(ymax, red[2][w]);
+        for (int w = 0; w < nw; ++w) ymax = nan_max(ymax, red[2][w]);
       }
-      const float scale = ymax / 448.0f;
+      // a NaN scale is stored as the positive quiet NaN; its reciprocal is
+      // NaN, so every code of the row is the NaN code; a zero row (scale 0)
+      // gets zero codes
+      float scale = ymax / 448.0f;
+      if (scale != scale) scale = __builtin_nanf("");
       if (tid == 0) static_cast<float*>(a.out_scale)[s] = scale;
-      inv = scale > 0.0f ? 1.0f / scale : 0.0f;
+      inv = scale == 0.0f ? 0.0f : 1.0f / scale;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -674,8 +701,16 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   const uintptr_t out_align = p->out_dtype == SP_FP8_E4M3 ? 8 : p->out_dtype == SP_FP4_E2M1 ? 4 : 16;
   if (out && misaligned(out, out_align))
     return fail(SP_ERR_ALIGN, "out %p is not %d-byte aligned", out, static_cast<int>(out_align));
+  // partials span (tp-1)*stride + S*H elements: no overflow, at most 2^47 bytes
   const int64_t stride = p->partial_stride ? p->partial_stride : S * H;
-  if ((stride * static_cast<int64_t>(elt_size(p->partial_dtype))) % 16 != 0)
+  const int64_t pe = static_cast<int64_t>(elt_size(p->partial_dtype));
+  int64_t span_elems, span_bytes;
+  if (__builtin_mul_overflow(tp - 1, stride, &span_elems) ||
+      __builtin_add_overflow(span_elems, S * H, &span_elems) ||
+      __builtin_mul_overflow(span_elems, pe, &span_bytes) || span_bytes > kMaxSpanBytes)
+    return fail(SP_ERR_SHAPE, "partials of tp=%lld with partial_stride=%lld span more than 2^47 bytes",
+                (long long)tp, (long long)stride);
+  if ((stride * pe) % 16 != 0)
     return fail(SP_ERR_ALIGN, "partial_stride=%lld elements is not a multiple of 16 bytes",
                 (long long)stride);
   if (out_scale && quant_mode != SP_QUANT_MX_BLOCK && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
@@ -688,37 +723,44 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
   plan->roff = (p->residual_rows == tp * S) ? r * S : 0;
   plan->doff = (deepstack && p->deepstack_rows == tp * S) ? r * S : 0;
 
-  // outputs must not overlap inputs (in-place residual excepted)
-  const size_t pe = elt_size(p->partial_dtype), ae = elt_size(p->act_dtype);
+  // No byte written by the call may be read by it or written twice: other
+  // workgroups may still be reading what one of them writes.  The one
+  // exception is the in-place update of the residual rows in use.
+  const size_t ae = elt_size(p->act_dtype);
   const size_t row_a = static_cast<size_t>(H) * ae;
   const char* res_used = static_cast<const char*>(residual) + plan->roff * row_a;
+  const void* res_written = p->residual_out ? p->residual_out : res_used;
+  const bool in_place = res_written == res_used;
   struct Span {
+    const char* name;
     const void* p;
     size_t n;
   };
   const Span ins[] = {
-      {partials, static_cast<size_t>((tp - 1) * stride + S * H) * pe},
-      {weight, row_a},
-      {bias, bias ? row_a : 0},
-      {deepstack, deepstack ? static_cast<size_t>(p->deepstack_rows) * row_a : 0},
-      {residual, static_cast<size_t>(p->residual_rows) * row_a},
+      {"partials", partials, static_cast<size_t>(span_bytes)},
+      {"weight", weight, row_a},
+      {"bias", bias, bias ? row_a : 0},
+      {"deepstack", deepstack, deepstack ? static_cast<size_t>(p->deepstack_rows) * row_a : 0},
+      {"residual", residual, static_cast<size_t>(p->residual_rows) * row_a},
+      {"the static scale", out_scale, quant_mode == SP_QUANT_STATIC_TENSOR ? sizeof(float) : 0},
   };
   const int64_t written_rows = (p->flags & SP_FLAG_VALID_ROWS_ONLY) ? plan->valid : S;
-  const size_t out_n = static_cast<size_t>(written_rows) * row_bytes_of(p->out_dtype, H);
-  for (const Span& in : ins)
-    if (overlap(out, out_n, in.p, in.n)) return fail(SP_ERR_SHAPE, "out overlaps an input");
-  if (p->residual_out && p->residual_out != res_used) {
-    const size_t ro_n = static_cast<size_t>(written_rows) * row_a;
-    for (const Span& in : ins)
-      if (overlap(p->residual_out, ro_n, in.p, in.n))
-        return fail(SP_ERR_SHAPE, "residual_out overlaps an input (pass NULL for in-place)");
-    if (overlap(p->residual_out, ro_n, out, out_n)) return fail(SP_ERR_SHAPE, "residual_out overlaps out");
-  }
-  if (scale_row_bytes_of(quant_mode, H) > 0 && out_scale) {
-    const size_t sn = static_cast<size_t>(written_rows) * scale_row_bytes_of(quant_mode, H);
-    for (const Span& in : ins)
-      if (overlap(out_scale, sn, in.p, in.n)) return fail(SP_ERR_SHAPE, "out_scale overlaps an input");
-    if (overlap(out_scale, sn, out, out_n)) return fail(SP_ERR_SHAPE, "out_scale overlaps out");
+  const Span outs[] = {
+      {in_place ? "the residual updated in place" : "residual_out", res_written,
+       static_cast<size_t>(written_rows) * row_a},
+      {"out", out, static_cast<size_t>(written_rows) * row_bytes_of(p->out_dtype, H)},
+      {"out_scale", out_scale, static_cast<size_t>(written_rows) * scale_row_bytes_of(quant_mode, H)},
+  };
+  constexpr int kResidualIn = 4;  // ins[] entry of the residual
+  for (int o = 0; o < 3; ++o) {
+    for (int k = 0; k < 6; ++k) {
+      if (o == 0 && in_place && k == kResidualIn) continue;
+      if (overlap(outs[o].p, outs[o].n, ins[k].p, ins[k].n))
+        return fail(SP_ERR_SHAPE, "%s overlaps %s", outs[o].name, ins[k].name);
+    }
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o].p, outs[o].n, outs[o2].p, outs[o2].n))
+        return fail(SP_ERR_SHAPE, "%s overlaps %s", outs[o].name, outs[o2].name);
   }
   return SP_OK;
 }

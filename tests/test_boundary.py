@@ -141,6 +141,41 @@ def test_invalid_problems_are_rejected(case, expect):
     assert msg and msg != "no error"
 
 
+RES_ROW = 4096 * 2   # bytes of one bf16 residual row of problem()
+FP8_STATIC = dict(quant_mode=sp.SP_QUANT_STATIC_TENSOR)
+
+
+@pytest.mark.parametrize("case,expect", [
+    # residual rows updated in place (residual_out NULL) inside the partials
+    (dict(a=dict(residual=BASE + 4096)), sp.SP_ERR_SHAPE),
+    # ... also when residual_out names those rows explicitly
+    (dict(p=dict(residual_out=BASE + 4096), a=dict(residual=BASE + 4096)), sp.SP_ERR_SHAPE),
+    # the in-place rows cover the weight, the bias or the deepstack
+    (dict(a=dict(residual=BASE + 2 * GB - 64 * RES_ROW)), sp.SP_ERR_SHAPE),
+    (dict(a=dict(bias=BASE + GB + 5 * RES_ROW)), sp.SP_ERR_SHAPE),
+    (dict(p=dict(deepstack_rows=128), a=dict(deepstack=BASE + GB + 64 * RES_ROW)), sp.SP_ERR_SHAPE),
+    # a replicated residual: only block tp_rank is written, block 0 may hold the weight
+    (dict(p=dict(residual_rows=1024), a=dict(weight=BASE + GB + 64)), sp.SP_OK),
+    (dict(p=dict(residual_rows=1024), a=dict(weight=BASE + GB + 7 * 128 * RES_ROW + 64)),
+     sp.SP_ERR_SHAPE),
+    # the static scale is read by every workgroup: not on out, nor on the residual written
+    (dict(p=dict(out_dtype=sp.SP_FP8_E4M3), a=dict(out_scale=BASE + 3 * GB + 64, **FP8_STATIC)),
+     sp.SP_ERR_SHAPE),
+    (dict(p=dict(out_dtype=sp.SP_FP8_E4M3), a=dict(out_scale=BASE + GB + 64, **FP8_STATIC)),
+     sp.SP_ERR_SHAPE),
+    (dict(p=dict(out_dtype=sp.SP_FP8_E4M3), a=dict(out_scale=BASE + 5 * GB, **FP8_STATIC)), sp.SP_OK),
+    # (tp-1)*partial_stride + S*H elements must be a span of at most 2^47 bytes
+    (dict(p=dict(partial_stride=2 ** 63 - 64)), sp.SP_ERR_SHAPE),       # wrapped to 0 before
+    (dict(p=dict(partial_stride=2 ** 62)), sp.SP_ERR_SHAPE),
+    (dict(p=dict(partial_stride=2 ** 43)), sp.SP_ERR_SHAPE),            # 7 * 2^44 bytes
+    (dict(p=dict(partial_stride=2 ** 42), a=dict(out=BASE - 2 ** 30, residual=BASE - 2 ** 31,
+                                                weight=BASE - 2 ** 32)), sp.SP_OK),
+])
+def test_written_bytes_may_not_be_read_or_span_too_far(case, expect):
+    status, msg = validate(problem(**case.get("p", {})), **case.get("a", {}))
+    assert status == expect, msg
+
+
 def test_out_alignment_is_the_store_width():
     """out needs the width of one lane's 8-element store: 16 bytes for bf16
     and f32, 8 for e4m3, 4 for packed e2m1 (MX scale bytes need none)."""

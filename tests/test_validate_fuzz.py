@@ -1,7 +1,10 @@
 """CPU: seeded perturbations of valid descriptors through sp_validate (host
 checks only, fake device addresses).  Every call returns a status, and
 every call the library accepts satisfies the rules include/sprms.h states
-for sp_reduce_add_rmsnorm's arguments."""
+for sp_reduce_add_rmsnorm's arguments -- including, with pointers moved into
+each other's buffers, that no byte the call writes is read by it or written
+twice (the in-place residual update excepted) and that the partials span at
+most 2^47 bytes."""
 
 import ctypes as C
 import math
@@ -40,6 +43,43 @@ def _valid(R):
     return p, q
 
 
+def _check_spans(p, q, ptr):
+    """The header's overlap and span rules, restated from its text."""
+    S, H, tp, r = p.shard_rows, p.hidden, p.tp, p.tp_rank
+    pe = 4 if p.partial_dtype == 0 else 2
+    ae = 4 if p.act_dtype == 0 else 2
+    stride = p.partial_stride or S * H
+    span = ((tp - 1) * stride + S * H) * pe
+    assert span <= 2 ** 47
+    v = max(0, min(S, p.num_tokens - r * S))
+    rows = v if p.flags & 1 else S
+    used = ptr["residual"] + (r * S if p.residual_rows == tp * S else 0) * H * ae
+    res_w = p.residual_out or used
+    in_place = res_w == used
+    orow = H // 2 if p.out_dtype == 3 else H * {0: 4, 1: 2, 2: 1}[p.out_dtype]
+    srow = 4 if q == 2 else (H // 32 if q == 4 else 0)
+    ins = {"partials": (ptr["partials"], span), "weight": (ptr["weight"], H * ae),
+           "bias": (ptr["bias"], H * ae if ptr["bias"] else 0),
+           "deepstack": (ptr["ds"], p.deepstack_rows * H * ae if ptr["ds"] else 0),
+           "residual": (ptr["residual"], p.residual_rows * H * ae),
+           "static scale": (ptr["osc"], 4 if q == 1 else 0)}
+    outs = {"residual written": (res_w, rows * H * ae), "out": (ptr["out"], rows * orow),
+            "out_scale": (ptr["osc"], rows * srow)}
+
+    def meet(a, b):
+        return bool(a[0] and b[0] and a[1] and b[1] and a[0] < b[0] + b[1] and b[0] < a[0] + a[1])
+
+    for o, ospan in outs.items():
+        for i, ispan in ins.items():
+            if o == "residual written" and i == "residual" and in_place:
+                continue
+            assert not meet(ospan, ispan), (o, i)
+    names = list(outs)
+    for a in range(3):
+        for b in range(a + 1, 3):
+            assert not meet(outs[names[a]], outs[names[b]]), (names[a], names[b])
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_accepted_calls_obey_the_header(seed):
     lib = sp.load()
@@ -64,8 +104,19 @@ def test_accepted_calls_obey_the_header(seed):
         out = 0x7F5000000000 + (R.choice([1, 2, 4, 8]) if R.random() < 0.05 else 0)
         osc = 0x7F6000000000 if q != 0 else None
         eps = R.choice([0.0, 1e-6, 1e-6, -1.0, float("nan")])
-        rc = lib.sp_validate(C.byref(p), partials, 0x7F2000000000, 0x7F3000000000, bias, C.c_float(eps), q,
-                             ds, out, osc)
+        ptr = dict(partials=partials, residual=0x7F2000000000, weight=0x7F3000000000, bias=bias,
+                   ds=ds, out=out, osc=osc)
+        if R.random() < 0.3:  # move one pointer into another buffer
+            k = R.choice(["residual", "weight", "bias", "ds", "out", "osc", "residual_out"])
+            base = R.choice([0x7F0000000000, 0x7F1000000000, 0x7F2000000000, 0x7F3000000000,
+                             0x7F4000000000, 0x7F5000000000, 0x7F6000000000])
+            at = base + 64 * R.choice([0, 1, 7, 1024, 1 << 20, 1 << 26])
+            if k == "residual_out":
+                p.residual_out = at
+            elif ptr[k] is not None:
+                ptr[k] = at
+        rc = lib.sp_validate(C.byref(p), ptr["partials"], ptr["residual"], ptr["weight"], ptr["bias"],
+                             C.c_float(eps), q, ptr["ds"], ptr["out"], ptr["osc"])
         assert rc in (0, -1, -2, -3, -4, -5), rc
         if rc != 0:
             continue
@@ -78,6 +129,7 @@ def test_accepted_calls_obey_the_header(seed):
         assert q in (0, 1, 2, 4) and p.flags in (0, 1)
         assert eps >= 0 and math.isfinite(eps) and math.isfinite(p.partial_scale)
         assert p.partial_stride == 0 or p.partial_stride >= p.shard_rows * p.hidden
-        assert partials is not None or p.shard_rows == 0  # S == 0 enqueues nothing
+        assert ptr["partials"] is not None or p.shard_rows == 0  # S == 0 enqueues nothing
         assert q != 4 or p.hidden % 32 == 0
+        _check_spans(p, q, ptr)
     assert accepted > N_CALLS // 10
