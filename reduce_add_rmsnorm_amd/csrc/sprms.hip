@@ -185,11 +185,23 @@ struct Vec<SP_F32> {
 // return the number and drop the NaN.
 __device__ __forceinline__ float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// Saturation to +-448 for numbers; a NaN becomes the positive quiet NaN, which
-// converts to the e4m3 NaN code 0x7F (fminf/fmaxf alone would turn it into
-// -448, a plausible-looking finite code).
+// Saturation to +-448 for numbers; a NaN stays a NaN (fminf/fmaxf alone would
+// turn it into -448, a plausible-looking finite code).
 __device__ __forceinline__ float sat_e4m3(float t) {
   return t == t ? fminf(fmaxf(t, -448.0f), 448.0f) : __builtin_nanf("");
+}
+
+// v_cvt_pk_fp8_f32 encodes a NaN as 0xFF (measured on gfx950, also for the
+// positive quiet NaN); the NaN code here is 0x7F, the one torch's
+// float8_e4m3fn cast writes.  Numbers are saturated to +-448 (0x7E / 0xFE)
+// before the conversion, so a 0xFF byte can only be a NaN: clear bit 7 of
+// every 0xFF byte of a packed word (x = ~w has a zero byte exactly there;
+// (x & 0x7F) + 0x7F sets bit 7 of a byte unless its low bits are zero, with
+// no carry out of the byte).
+__device__ __forceinline__ uint32_t nan_code_7f(uint32_t w) {
+  const uint32_t x = ~w;
+  const uint32_t ff_bytes = ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu);
+  return w ^ ff_bytes;
 }
 
 // 8 fp32 -> 8 OCP e4m3fn codes (little-endian byte order = element order),
@@ -202,7 +214,7 @@ __device__ __forceinline__ u32x2 pack_e4m3(const float (&t)[kVec]) {
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-  return u32x2{static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+  return u32x2{nan_code_7f(static_cast<uint32_t>(lo)), nan_code_7f(static_cast<uint32_t>(hi))};
 }
 
 __device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, u32x2 v) {
