@@ -8,7 +8,8 @@ workload's timed rank (every stage of the path in one kernel), inputs
 already resident in HBM.  Prints one JSON line: whole-job HBM throughput
 over the algorithmic bytes (GB/s), the roofline of the kernel (per-launch
 HIP-event durations on the launch stream), and the CPU oracle timed on a
-bounded sample of the same shard.
+bounded sample of the same shard.  The default run (C5, the headline) also
+times C4 with the same protocol and reports it under "also".
 """
 
 from __future__ import annotations
@@ -433,6 +434,66 @@ def cpu_baseline(path: str, w, x, budget_s: float, threads: int, *, nbytes=None,
     }
 
 
+def time_plain(launch, stream, steps):
+    """K back-to-back launches bracketed by HIP events on the launch stream and
+    by the host clock between two synchronisations, then a short pass with an
+    event pair per launch for the spread.  Returns (mean kernel ms from the
+    events, wall ms per step, per-launch ms list)."""
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / steps
+    n_spread = min(steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
+    for i in range(n_spread):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return avg_ms, wall * 1000.0 / steps, [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+
+
+def also_fused(name, args, dev):
+    """Another workload's fused kernel, timed with the headline's protocol
+    (same warm-up and step count), for the same JSON line."""
+    w = WORKLOADS[name]
+    x, launch, bufs = setup(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    avg_ms, ms_per_step, per = time_plain(launch, stream, args.steps)
+    nbytes = w.algorithmic_bytes()
+    achieved = nbytes / (avg_ms / 1000.0) / 1e9
+    rec = {
+        "workload": f"{w.name}: {w.description}",
+        "tp": w.tp, "rank": w.rank, "shard_rows": w.shard_rows, "hidden": w.hidden,
+        "quant": QUANT_NAMES[w.quant_mode],
+        "algorithmic_bytes": nbytes,
+        "ms_per_step": round(ms_per_step, 6),
+        "value_gbs": round(nbytes / (ms_per_step / 1000.0) / 1e9, 2),
+        "shard_tokens_per_s": round(w.valid_rows() / (ms_per_step / 1000.0), 1),
+        "kernel_us": {"mean": round(avg_ms * 1000, 2),
+                      "median_single": round(statistics.median(per) * 1000, 2),
+                      "p10": round(float(np.percentile(per, 10)) * 1000, 2),
+                      "p90": round(float(np.percentile(per, 90)) * 1000, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, "fused")},
+    }
+    del x, launch, bufs
+    torch.cuda.empty_cache()
+    return rec
+
+
 def copy_calibration(args, dev):
     """A device-to-device copy of known size: every launch reads and writes
     exactly n bytes, which fixes the scale of FETCH_SIZE / WRITE_SIZE."""
@@ -480,6 +541,10 @@ def main():
                     help="fused path: replace the workload's output quantisation by block "
                          "scaling (32-element E8M0 scales) with e4m3 or e2m1 elements; gemm "
                          "path: fp8 times the e4m3 producer (sp_scaled_matmul_scatter)")
+    ap.add_argument("--also", default=None, metavar="W[,W...]",
+                    help="fused path: further workloads timed after the headline with the same "
+                         "protocol and reported under 'also' in the same line (default: C4 "
+                         "when the headline is the default C5 run; '' for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling hardware byte counters)")
@@ -571,29 +636,7 @@ def main():
     elif not args.cold:
         # timed region: K back-to-back launches, HIP events on the launch stream
         # at both ends, host clock between two synchronisations
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            launch()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        avg_ms = ev0.elapsed_time(ev1) / args.steps
-
-        # launch-duration spread from a short pass with an event pair per launch
-        n_spread = min(args.steps, 50)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread)]
-        for i in range(n_spread):
-            starts[i].record(stream)
-            launch()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        per_launch_ms = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
-        ms_per_step = wall * 1000.0 / args.steps
+        avg_ms, ms_per_step, per_launch_ms = time_plain(launch, stream, args.steps)
     else:
         # cache-cold: before every launch a read+write pass over 512 MiB (twice
         # the Infinity Cache) on the same stream, outside the launch's events
@@ -677,6 +720,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    also = args.also
+    if also is None:
+        also = ("C4" if args.path == "fused" and args.workload == "C5" and not args.quant
+                and not args.graph and not args.cold else "")
+    if also:
+        if args.path != "fused" or args.quant or args.graph or args.cold:
+            ap.error("--also goes with the plain fused path")
+        result["also"] = {n: also_fused(n, args, dev) for n in also.split(",") if n}
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(args.path, w, x, args.cpu_budget, max(1, args.cpu_threads),
                                               nbytes=nbytes, fp8_gemm=fp8_gemm)
