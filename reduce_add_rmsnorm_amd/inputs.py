@@ -1,9 +1,14 @@
 """Seeded synthetic inputs for the shard path, shared by tests and the benchmark.
 
 This module holds shapes, distributions and random draws only: none of the
-path's arithmetic.  Values come from torch's seeded generator on the device
-that will hold them, drawn as float32 N(mu, sigma) and rounded once to the
-storage dtype (torch's cast, round to nearest even).
+path's arithmetic.  Values come from a counter-based generator written in
+plain C (inputs_gen.c, run on host threads): element (row, column) of a
+tensor is SplitMix64 of its position under a key made from the seed, the
+tensor and the source rank, turned into N(0, 1) by Box-Muller, then
+mu + sigma * z rounded once to f32 (and f32 to bf16, nearest even).  Rows are
+global token indices, so rank r's shard of partial q is rows [r*S, (r+1)*S)
+of partial q's full tensor, and any rows can be drawn on any machine, with or
+without a GPU; tensors for a device are drawn on the host and copied.
 
 Workloads (one rank's shard each; shapes follow the pages' worked examples
 where they give one -- vllm-ascend PR #18671 walkthrough §2: 3500 tokens
@@ -18,9 +23,13 @@ padded to 3504 over TP=16, 219 tokens per rank, hidden 8192):
 
 from __future__ import annotations
 
+import ctypes
 import dataclasses
+import os
+import subprocess
 from typing import Optional
 
+import numpy as np
 import torch
 
 QUANT_NONE, QUANT_STATIC_TENSOR, QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK = 0, 1, 2, 4
@@ -114,19 +123,57 @@ WORKLOADS = {
 }
 
 
-def _normal(shape, mu, sigma, dtype, device, seed):
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    if sigma != 1.0:
-        t.mul_(sigma)
-    if mu != 0.0:
-        t.add_(mu)
-    return t if dtype == torch.float32 else t.to(dtype)
+_HERE = os.path.dirname(os.path.abspath(__file__))
+GEN_SRC = os.path.join(_HERE, "inputs_gen.c")
+GEN_LIB = os.path.join(_HERE, "libsprms_inputs.so")
+GEN_CMD = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-pthread", "-o", GEN_LIB,
+           GEN_SRC, "-lm"]
+_gen = None
 
 
-def _seed(w: Workload, rank: int, tid: int, base: int) -> int:
-    return ((base + w.seed_index) * 131 + rank) * 17 + tid
+def build_generator() -> str:
+    """Compile the input generator with gcc (always; part of the repository build)."""
+    subprocess.run(GEN_CMD, check=True)
+    return GEN_LIB
+
+
+def _lib():
+    global _gen
+    if _gen is None:
+        if not os.path.exists(GEN_LIB):
+            build_generator()
+        lib = ctypes.CDLL(GEN_LIB)
+        lib.sprms_inputs_key.argtypes = [ctypes.c_uint64] * 3
+        lib.sprms_inputs_key.restype = ctypes.c_uint64
+        lib.sprms_inputs_normal.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_int]
+        lib.sprms_inputs_normal.restype = ctypes.c_int
+        _gen = lib
+    return _gen
+
+
+GEN_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def draw(seed: int, tensor: int, source: int, row0: int, rows: int, cols: int, mu: float, sigma: float,
+         dtype: torch.dtype, out: Optional[np.ndarray] = None) -> torch.Tensor:
+    """Rows [row0, row0 + rows) of a [.][cols] tensor of the stream
+    (seed, tensor, source), as a CPU tensor of dtype (float32 or bfloat16),
+    drawn into `out` (a C-contiguous [rows][cols] array of the storage type)
+    when given."""
+    lib = _lib()
+    bf16 = dtype == torch.bfloat16
+    arr = np.empty((rows, cols), np.uint16 if bf16 else np.float32) if out is None else out
+    assert arr.shape == (rows, cols) and arr.dtype == (np.uint16 if bf16 else np.float32)
+    assert arr.flags["C_CONTIGUOUS"]
+    key = lib.sprms_inputs_key(seed, tensor, source)
+    rc = lib.sprms_inputs_normal(key, row0, rows, cols, float(mu), float(sigma), int(bf16),
+                                 arr.ctypes.data_as(ctypes.c_void_p), GEN_THREADS)
+    if rc != 0:
+        raise ValueError(f"input draw failed for rows {row0}+{rows} x {cols}")
+    t = torch.from_numpy(arr)
+    return t.view(torch.int16).view(torch.bfloat16) if bf16 else t
 
 
 def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed=BASE_SEED,
@@ -144,19 +191,25 @@ def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed
     r = w.rank if rank is None else rank
     S = w.shard_rows if shard_rows is None else shard_rows
     H, tp = w.hidden, w.tp
+    seed = base_seed + w.seed_index
+    # partial q of rank r: rows [r*S, (r+1)*S) of partial q's full tensor
+    pbuf = np.empty((tp, S, H), np.uint16 if w.partial_dtype == torch.bfloat16 else np.float32)
+    for q in range(tp):
+        draw(seed, _TID_PARTIALS, q, r * S, S, H, 0.0, w.partial_sigma, w.partial_dtype, out=pbuf[q])
+    parts = torch.from_numpy(pbuf)
+    if w.partial_dtype == torch.bfloat16:
+        parts = parts.view(torch.int16).view(torch.bfloat16)
+    res0, res_rows = (0, tp * S) if w.residual_replicated else (r * S, S)
     out = {
-        "partials": _normal((tp, S, H), 0.0, w.partial_sigma, w.partial_dtype, device,
-                            _seed(w, r, _TID_PARTIALS, base_seed)),
-        "residual": _normal(((tp * S) if w.residual_replicated else S, H), 0.0, w.residual_sigma,
-                            w.act_dtype, device, _seed(w, r, _TID_RESIDUAL, base_seed)),
-        # gain and bias are replicated on every rank: their seed has no rank
-        "weight": _normal((H,), w.weight_mu, w.weight_sigma, w.act_dtype, device,
-                          _seed(w, 0, _TID_WEIGHT, base_seed)),
-        "bias": (_normal((H,), 0.0, w.bias_sigma, w.act_dtype, device,
-                         _seed(w, 0, _TID_BIAS, base_seed)) if w.bias else None),
-        "deepstack": (_normal((tp * S, H), 0.0, w.deepstack_sigma, w.act_dtype, device,
-                              _seed(w, r, _TID_DEEPSTACK, base_seed)) if w.deepstack else None),
+        "partials": parts,
+        "residual": draw(seed, _TID_RESIDUAL, 0, res0, res_rows, H, 0.0, w.residual_sigma, w.act_dtype),
+        # gain and bias are replicated on every rank: one row each, no rank in the stream
+        "weight": draw(seed, _TID_WEIGHT, 0, 0, 1, H, w.weight_mu, w.weight_sigma, w.act_dtype)[0],
+        "bias": (draw(seed, _TID_BIAS, 0, 0, 1, H, 0.0, w.bias_sigma, w.act_dtype)[0] if w.bias else None),
+        "deepstack": (draw(seed, _TID_DEEPSTACK, 0, 0, tp * S, H, 0.0, w.deepstack_sigma, w.act_dtype)
+                      if w.deepstack else None),
     }
+    out = {k: (None if t is None else t.to(device)) for k, t in out.items()}
     if pad_fill is not None:
         T = min(w.num_tokens, tp * S) if num_tokens is None else num_tokens
         v = max(0, min(S, T - r * S))

@@ -38,7 +38,9 @@ def test_ranks_differ_but_gain_and_bias_are_replicated(name):
     w = _small(name)
     a, b = make_inputs(w, rank=0), make_inputs(w, rank=1)
     assert not torch.equal(a["partials"], b["partials"])
-    assert not torch.equal(a["residual"], b["residual"])
+    # a replicated residual is the same full tensor on every rank; a shard
+    # residual holds the rank's own rows
+    assert torch.equal(a["residual"], b["residual"]) == w.residual_replicated
     assert torch.equal(a["weight"], b["weight"])
     if w.bias:
         assert torch.equal(a["bias"], b["bias"])
@@ -109,3 +111,77 @@ def test_algorithmic_bytes_of_the_timed_workloads():
     c2 = WORKLOADS["C2"]
     S2, H2, v2 = 128, 4096, 1000 - 7 * 128
     assert c2.algorithmic_bytes() == v2 * H2 * (8 * 2 + 2) + H2 * 2 + S2 * H2 * (2 + 2)
+
+
+# ------------------------------------------------ the counter-based generator
+
+from reduce_add_rmsnorm_amd import inputs as I  # noqa: E402
+
+M64 = (1 << 64) - 1
+
+
+def _mix64(z):
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
+    return z ^ (z >> 31)
+
+
+def _reference_value(seed, tensor, source, row, col, cols, mu, sigma):
+    """The recipe of inputs_gen.c restated in Python (integers exact, the
+    transcendental part in double, so equal to the single-precision draw to
+    ~1e-6)."""
+    import math
+    key = _mix64((_mix64(seed) + tensor * 0xD1B54A32D192ED03 + source * 0xABC98388FB8FAC03) & M64)
+    e = row * cols + col
+    u = _mix64((key + ((e >> 1) + 1) * 0x9E3779B97F4A7C15) & M64)
+    u1 = ((u >> 40) + 1) / 2.0 ** 24
+    u2 = (u & 0xFFFFFF) / 2.0 ** 24
+    r = math.sqrt(-2.0 * math.log(u1))
+    z = r * (math.sin(2 * math.pi * u2) if e & 1 else math.cos(2 * math.pi * u2))
+    return mu + sigma * z
+
+
+def test_generator_follows_its_stated_recipe():
+    seed, cols = 20261206, 40
+    t = I.draw(seed, 1, 3, 1000, 5, cols, 0.25, 0.5, torch.float32)
+    for row in range(5):
+        for col in (0, 1, 2, 17, 38, 39):
+            want = _reference_value(seed, 1, 3, 1000 + row, col, cols, 0.25, 0.5)
+            assert abs(float(t[row, col]) - want) < 2e-5, (row, col)
+    # bf16 storage is the f32 draw rounded to nearest even
+    b = I.draw(seed, 1, 3, 1000, 5, cols, 0.25, 0.5, torch.bfloat16)
+    assert torch.equal(b, t.to(torch.bfloat16))
+
+
+def test_generator_rows_are_independent_of_the_call():
+    # any row range, any thread count: the same bytes for the same positions
+    full = I.draw(7, 2, 0, 0, 300, 64, 0.0, 1.0, torch.bfloat16)
+    part = I.draw(7, 2, 0, 123, 77, 64, 0.0, 1.0, torch.bfloat16)
+    assert torch.equal(part.view(torch.int16), full[123:200].view(torch.int16))
+    saved = I.GEN_THREADS
+    try:
+        I.GEN_THREADS = 1
+        one = I.draw(7, 2, 0, 0, 300, 64, 0.0, 1.0, torch.bfloat16)
+    finally:
+        I.GEN_THREADS = saved
+    assert torch.equal(one.view(torch.int16), full.view(torch.int16))
+    # another tensor id, source or seed: another stream
+    assert not torch.equal(I.draw(7, 3, 0, 0, 300, 64, 0.0, 1.0, torch.bfloat16), full)
+    assert not torch.equal(I.draw(7, 2, 1, 0, 300, 64, 0.0, 1.0, torch.bfloat16), full)
+    assert not torch.equal(I.draw(8, 2, 0, 0, 300, 64, 0.0, 1.0, torch.bfloat16), full)
+
+
+@pytest.mark.parametrize("name", ["C2", "C5"])
+def test_rank_shards_are_slices_of_the_full_tensors(name):
+    # partial q of rank r is rows [r*S, (r+1)*S) of partial q's full tensor, so
+    # the ranks' shards of one workload fit together into the whole layer
+    w = _small(name)
+    S, H, tp = w.shard_rows, w.hidden, w.tp
+    full = {q: I.draw(I.BASE_SEED + w.seed_index, 1, q, 0, tp * S, H, 0.0, w.partial_sigma, w.partial_dtype)
+            for q in range(tp)}
+    for r in (0, tp - 1):
+        x = make_inputs(w, rank=r)
+        for q in range(tp):
+            assert torch.equal(x["partials"][q].view(torch.int16), full[q][r * S:(r + 1) * S].view(torch.int16))
+        if w.deepstack:   # the full deepstack is the same on every rank
+            assert torch.equal(x["deepstack"], make_inputs(w, rank=0)["deepstack"])
