@@ -172,6 +172,8 @@ def draw(seed: int, tensor: int, source: int, row0: int, rows: int, cols: int, m
                                  arr.ctypes.data_as(ctypes.c_void_p), GEN_THREADS)
     if rc != 0:
         raise ValueError(f"input draw failed for rows {row0}+{rows} x {cols}")
+    if arr.size == 0:  # numpy gives empty arrays zero strides; keep torch's row-major ones
+        return torch.empty((rows, cols), dtype=dtype)
     t = torch.from_numpy(arr)
     return t.view(torch.int16).view(torch.bfloat16) if bf16 else t
 
@@ -199,6 +201,8 @@ def make_inputs(w: Workload, rank: Optional[int] = None, device="cpu", base_seed
     parts = torch.from_numpy(pbuf)
     if w.partial_dtype == torch.bfloat16:
         parts = parts.view(torch.int16).view(torch.bfloat16)
+    if S == 0:  # numpy gives empty arrays zero strides; keep torch's row-major ones
+        parts = torch.empty((tp, 0, H), dtype=w.partial_dtype)
     res0, res_rows = (0, tp * S) if w.residual_replicated else (r * S, S)
     out = {
         "partials": parts,

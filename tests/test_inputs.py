@@ -185,3 +185,14 @@ def test_rank_shards_are_slices_of_the_full_tensors(name):
             assert torch.equal(x["partials"][q].view(torch.int16), full[q][r * S:(r + 1) * S].view(torch.int16))
         if w.deepstack:   # the full deepstack is the same on every rank
             assert torch.equal(x["deepstack"], make_inputs(w, rank=0)["deepstack"])
+
+
+@pytest.mark.parametrize("name", ["C2", "C5"])
+def test_an_empty_shard_has_row_major_strides(name):
+    # S = 0: the tensors are empty but strided like any [tp][S][H] block, which
+    # the binding checks before it hands pointers to the library
+    w = _small(name)
+    x = make_inputs(w, rank=0, shard_rows=0, num_tokens=0)
+    assert x["partials"].shape == (w.tp, 0, w.hidden)
+    assert x["partials"].stride() == torch.empty((w.tp, 0, w.hidden)).stride()
+    assert x["residual"].stride() == torch.empty((0, w.hidden)).stride()
