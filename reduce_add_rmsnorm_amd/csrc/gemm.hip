@@ -374,8 +374,9 @@ int launch_matmul(const sp_matmul_problem* p, const void* x, const float* x_scal
   if (p->out_dtype != SP_BF16 && p->out_dtype != SP_F32)
     return fail(SP_ERR_DTYPE, "out_dtype=%d must be SP_BF16 or SP_F32", p->out_dtype);
   const int64_t S = p->shard_rows, K = p->k, N = p->n;
+  // bound S before multiplying, so that tp*S cannot wrap past the check
+  if (S < 0 || S > INT32_MAX / tp) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
   const int64_t M = S * tp;
-  if (S < 0 || M > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
   const int64_t kq = fp8 ? 16 : 8;  // K elements per 16-byte chunk
   if (K < kq || K % kq != 0 || K > (1 << 20))
     return fail(SP_ERR_SHAPE, "k=%lld must be a multiple of %lld in [%lld, 2^20]", (long long)K, (long long)kq,

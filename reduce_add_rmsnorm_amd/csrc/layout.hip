@@ -318,7 +318,7 @@ int sp_fc2_regroup(const sp_fc2_problem* f, const void* const* src, void* const*
   if (N < 0 || N % G != 0 || N > INT32_MAX)
     return fail(SP_ERR_SHAPE, "tokens=%lld must be a multiple of %d below 2^31", (long long)N, G);
   const int odp = G / P;
-  if (C < 1 || (C * static_cast<int64_t>(e)) % 4 != 0 || C * static_cast<int64_t>(e) * odp > (1ll << 30))
+  if (C < 1 || C > (1ll << 30) / (static_cast<int64_t>(e) * odp) || (C * static_cast<int64_t>(e)) % 4 != 0)
     return fail(SP_ERR_SHAPE, "cols=%lld: rows must be a multiple of 4 bytes and at most 1 GiB", (long long)C);
   const int first = f->rank < 0 ? 0 : f->rank, nranks = f->rank < 0 ? G : 1;
   const int64_t rows = static_cast<int64_t>(nranks) * (N / odp);
@@ -361,8 +361,9 @@ int sp_dsacp_heads_to_tokens(const sp_dsacp_problem* f, const void* const* attn,
   const size_t e = elt_size(f->dtype);
   if (e == 0) return fail(SP_ERR_DTYPE, "dtype=%d unsupported", f->dtype);
   const int64_t S = f->shard_rows, D = f->head_cols;
-  if (S < 0 || S * tp > INT32_MAX) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
-  if (D < 1 || (D * static_cast<int64_t>(e)) % 4 != 0 || D * static_cast<int64_t>(e) * tp > (1ll << 30))
+  // bound S before multiplying, so that tp*S cannot wrap past the check
+  if (S < 0 || S > INT32_MAX / tp) return fail(SP_ERR_SHAPE, "shard_rows=%lld: need 0 <= tp*S < 2^31", (long long)S);
+  if (D < 1 || D > (1ll << 30) / (static_cast<int64_t>(e) * tp) || (D * static_cast<int64_t>(e)) % 4 != 0)
     return fail(SP_ERR_SHAPE, "head_cols=%lld: rows must be a multiple of 4 bytes and at most 1 GiB", (long long)D);
   const int first = f->rank < 0 ? 0 : f->rank, nranks = f->rank < 0 ? tp : 1;
   const int64_t rows = static_cast<int64_t>(nranks) * tp * S;

@@ -485,3 +485,35 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+# sizes so large that multiplying them first would wrap int64 past the range
+# checks: each must be rejected, never accepted as a small or empty problem
+TP64 = dict(tp=64, dst=[BASE + (2 + r) * GB for r in range(64)])
+
+
+@pytest.mark.parametrize("case", [
+    dict(TP64, S=1 << 58),            # 64 * 2^58 = 2^64 wraps to 0
+    dict(TP64, S=(1 << 57) + 1),      # wraps negative
+    dict(S=(1 << 62) + 3),            # tp = 4: wraps to 12
+])
+def test_matmul_scatter_rejects_shard_rows_that_would_wrap(case):
+    status, msg = _mm(**case)
+    assert status == sp.SP_ERR_SHAPE, msg
+
+
+@pytest.mark.parametrize("case", [
+    dict(tp=64, S=1 << 58, attn=[BASE + q * GB for q in range(64)], out=[BASE + (64 + q) * GB for q in range(64)]),
+    dict(S=(1 << 62) + 2),
+    dict(D=1 << 62),                  # head_cols * 2 bytes * tp wraps
+    dict(D=(1 << 61) + 2),
+])
+def test_dsacp_rejects_sizes_that_would_wrap(case):
+    status, msg = _dsacp(**case)
+    assert status == sp.SP_ERR_SHAPE, msg
+
+
+@pytest.mark.parametrize("Cc", [1 << 62, (1 << 61) + 2, (1 << 60) + 2])
+def test_fc2_rejects_cols_that_would_wrap(Cc):
+    status, msg = _fc2(Cc=Cc)
+    assert status == sp.SP_ERR_SHAPE, msg
