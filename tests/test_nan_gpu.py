@@ -198,3 +198,36 @@ def test_nan_gain_or_bias_element_reaches_its_column(dev, mode, which):
         _same_bytes(got["out"][:, rest], clean["out"][:, rest])
         sc_rest = np.arange(H // 32) != 1
         _same_bytes(got["out_scale"][:, sc_rest], clean["out_scale"][:, sc_rest])
+
+
+# The maxima run in other code paths for a runtime partial count (tp = 5,
+# partials loaded in groups) and for rows of more than 8192 elements (4 or 8
+# vectors per thread): the NaN rule must hold there too.
+@pytest.mark.parametrize("tp,H", [(5, 1024), (4, 16384), (3, 32768)])
+@pytest.mark.parametrize("mode", ["per_token", "per_token_bias", "mxfp8", "static"])
+def test_nan_rule_in_every_kernel_shape(dev, tp, H, mode):
+    say(f"NaN rule at tp={tp} H={H} mode {mode}")
+    quant, out_t, od, bias = MODES[mode]
+    S = 6
+    w = dataclasses.replace(WORKLOADS["C5"], tp=tp, num_tokens=tp * S - 2, num_tokens_pad=tp * S, hidden=H,
+                            quant_mode=quant, out_dtype=out_t, bias=bias, deepstack=True)
+    rank = tp - 1
+    x = make_inputs(w, rank=rank, device=dev, pad_fill=float("nan"))
+    x["partials"][tp - 1, 1, H - 3] = float("nan")   # valid row 1, last partial, near the row's end
+    res_out = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((S, H), dtype=torch.uint8, device=dev)
+    scale = (torch.tensor([STATIC_SCALE], device=dev) if quant == QUANT_STATIC_TENSOR else
+             torch.empty((S,), device=dev) if quant == QUANT_DYNAMIC_TOKEN else
+             torch.empty((S, H // 32), dtype=torch.uint8, device=dev))
+    sp.sp_reduce_add_rmsnorm(x["partials"], x["residual"], x["weight"], x["bias"], 1e-6, quant,
+                             x["deepstack"], out, scale, tp_rank=rank, num_tokens=w.num_tokens,
+                             residual_out=res_out)
+    torch.cuda.synchronize()
+    h = {k: to_host(t) for k, t in x.items()}
+    ref = oracle.reduce_add_rmsnorm(h["partials"], h["residual"], h["weight"], h["bias"], 1e-6, quant,
+                                    h["deepstack"], tp_rank=rank, num_tokens=w.num_tokens, out_dtype=od,
+                                    static_scale=STATIC_SCALE, rows=[1])
+    _same_bytes(to_host(out)[1], ref["out"][0])
+    if quant != QUANT_STATIC_TENSOR:
+        _same_bytes(scale.cpu().numpy()[1], ref["out_scale"][0])
+    assert np.isnan(bf16_bits_to_f64(to_host(res_out)[1, H - 3]))
