@@ -722,7 +722,9 @@ int check(const sp_problem* p, const void* partials, const void* residual, const
       __builtin_mul_overflow(span_elems, pe, &span_bytes) || span_bytes > kMaxSpanBytes)
     return fail(SP_ERR_SHAPE, "partials of tp=%lld with partial_stride=%lld span more than 2^47 bytes",
                 (long long)tp, (long long)stride);
-  if ((stride * pe) % 16 != 0)
+  // (stride * pe) % 16, in a form that cannot overflow: with tp = 1 the span
+  // check above leaves the stride unbounded
+  if (((stride % 16) * pe) % 16 != 0)
     return fail(SP_ERR_ALIGN, "partial_stride=%lld elements is not a multiple of 16 bytes",
                 (long long)stride);
   if (out_scale && quant_mode != SP_QUANT_MX_BLOCK && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
@@ -811,7 +813,8 @@ int sp_reduce_add_rmsnorm(const sp_problem* p, const void* partials, void* resid
   ka.deepstack = deepstack ? static_cast<const char*>(deepstack) + plan.doff * H * ae : nullptr;
   ka.out = out;
   ka.out_scale = out_scale;
-  ka.plane = p->partial_stride ? p->partial_stride : p->shard_rows * H;
+  // with one partial the stride addresses nothing (and is not bounded by the span check)
+  ka.plane = p->tp == 1 ? 0 : p->partial_stride ? p->partial_stride : p->shard_rows * H;
   ka.H = static_cast<int32_t>(H);
   ka.nvec = static_cast<int32_t>(H / kVec);
   ka.valid = static_cast<int32_t>(plan.valid);

@@ -190,6 +190,18 @@ def test_out_alignment_is_the_store_width():
         assert status == want, (dt, off, msg)
 
 
+def test_one_partial_takes_any_stride_without_overflow():
+    # with tp = 1 the stride addresses nothing, so the span check cannot bound
+    # it; the alignment test must still hold without forming stride * 2 (the
+    # products below overflow int64)
+    one = dict(tp=1, tp_rank=0, num_tokens=128)
+    assert validate(problem(partial_stride=2 ** 62, **one))[0] == sp.SP_OK
+    assert validate(problem(partial_stride=2 ** 63 - 8, **one))[0] == sp.SP_OK
+    assert validate(problem(partial_stride=2 ** 63 - 1, **one))[0] == sp.SP_ERR_ALIGN
+    assert validate(problem(partial_stride=2 ** 62 + 4, partial_dtype=sp.SP_F32, **one))[0] == sp.SP_OK
+    assert validate(problem(partial_stride=2 ** 62 + 2, partial_dtype=sp.SP_F32, **one))[0] == sp.SP_ERR_ALIGN
+
+
 def test_strided_and_valid_rows_only_problems_pass():
     assert validate(problem(partial_stride=1024 * 4096))[0] == sp.SP_OK
     assert validate(problem(flags=sp.SP_FLAG_VALID_ROWS_ONLY))[0] == sp.SP_OK
