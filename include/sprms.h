@@ -209,7 +209,8 @@ typedef struct {
  *
  * Bytes are copied unchanged (bit-exact).  Same error convention as
  * sp_reduce_add_rmsnorm: every check runs before anything is enqueued, and
- * out must not overlap a shard.  T == 0 enqueues nothing.
+ * neither out nor out_scale may overlap a shard, a shard's scales or each
+ * other (SP_ERR_SHAPE).  T == 0 enqueues nothing.
  */
 int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
                         const void* const* shard_scales, void* out, void* out_scale,

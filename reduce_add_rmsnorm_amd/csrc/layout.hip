@@ -269,21 +269,28 @@ int sp_all_gather_unpad(const sp_gather_problem* g, const void* const* shards,
   if (out_scale && sb == 4 && (reinterpret_cast<uintptr_t>(out_scale) & 3u))
     return fail(SP_ERR_ALIGN, "out_scale %p is not 4-byte aligned", out_scale);
   const size_t out_n = static_cast<size_t>(T) * row_bytes;
+  const size_t out_scale_n = static_cast<size_t>(T * sb), shard_n = static_cast<size_t>(S) * row_bytes,
+               shard_scale_n = static_cast<size_t>(S * sb);
+  // nothing written may be read by the call or written twice
+  if (overlap(out, out_n, out_scale, out_scale_n)) return fail(SP_ERR_SHAPE, "out overlaps out_scale");
   GArgs ga;
   memset(&ga, 0, sizeof ga);
   for (int q = 0; q < g->tp; ++q) {
     if (!shards[q]) return fail(SP_ERR_NULL, "shards[%d] is NULL", q);
     if (reinterpret_cast<uintptr_t>(shards[q]) & amask)
       return fail(SP_ERR_ALIGN, "shards[%d] %p is not %d-byte aligned", q, shards[q], B);
-    if (overlap(out, out_n, shards[q], static_cast<size_t>(S) * row_bytes))
-      return fail(SP_ERR_SHAPE, "out overlaps shards[%d]", q);
+    if (overlap(out, out_n, shards[q], shard_n)) return fail(SP_ERR_SHAPE, "out overlaps shards[%d]", q);
+    if (overlap(out_scale, out_scale_n, shards[q], shard_n))
+      return fail(SP_ERR_SHAPE, "out_scale overlaps shards[%d]", q);
     ga.src[q] = static_cast<const char*>(shards[q]);
     if (shard_scales) {
       if (!shard_scales[q]) return fail(SP_ERR_NULL, "shard_scales[%d] is NULL", q);
       if (sb == 4 && (reinterpret_cast<uintptr_t>(shard_scales[q]) & 3u))
         return fail(SP_ERR_ALIGN, "shard_scales[%d] is not 4-byte aligned", q);
-      if (overlap(out_scale, static_cast<size_t>(T * sb), shard_scales[q], static_cast<size_t>(S * sb)))
+      if (overlap(out_scale, out_scale_n, shard_scales[q], shard_scale_n))
         return fail(SP_ERR_SHAPE, "out_scale overlaps shard_scales[%d]", q);
+      if (overlap(out, out_n, shard_scales[q], shard_scale_n))
+        return fail(SP_ERR_SHAPE, "out overlaps shard_scales[%d]", q);
       ga.ssrc[q] = static_cast<const char*>(shard_scales[q]);
     }
   }

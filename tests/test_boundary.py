@@ -212,10 +212,10 @@ def test_strided_and_valid_rows_only_problems_pass():
 
 
 def _gather(tp=2, S=4, H=16, T=8, dtype=sp.SP_BF16, shards=None, scales=None, out=BASE + 8 * GB,
-            out_scale=None):
+            out_scale=None, sb=0):
     import ctypes as C
     lib = sp.load()
-    g = sp.sp_gather_problem(tp=tp, dtype=dtype, shard_rows=S, hidden=H, num_tokens=T)
+    g = sp.sp_gather_problem(tp=tp, dtype=dtype, shard_rows=S, hidden=H, num_tokens=T, scale_row_bytes=sb)
     shards = shards if shards is not None else [BASE + q * GB for q in range(tp)]
     src = (C.c_void_p * len(shards))(*shards)
     ssrc = None if scales is None else (C.c_void_p * len(scales))(*scales)
@@ -234,6 +234,12 @@ def _gather(tp=2, S=4, H=16, T=8, dtype=sp.SP_BF16, shards=None, scales=None, ou
     (dict(out=BASE + 64), sp.SP_ERR_SHAPE),                        # out overlaps shard 0
     (dict(scales=[BASE + 4 * GB, BASE + 5 * GB]), sp.SP_ERR_NULL),  # no out_scale
     (dict(out_scale=BASE + 6 * GB), sp.SP_ERR_NULL),                # no shard scales
+    # with scales (4 bytes a row): nothing written may overlap what is read, or each other
+    # (only rejections here: an accepted call would launch on these fake addresses)
+    (dict(sb=4, scales=[BASE + 4 * GB, BASE + 5 * GB], out_scale=BASE + GB + 16), sp.SP_ERR_SHAPE),
+    (dict(sb=4, scales=[BASE + 4 * GB, BASE + 8 * GB + 64], out_scale=BASE + 6 * GB), sp.SP_ERR_SHAPE),
+    (dict(sb=4, scales=[BASE + 4 * GB, BASE + 5 * GB], out_scale=BASE + 8 * GB + 240), sp.SP_ERR_SHAPE),
+    (dict(sb=4, scales=[BASE + 4 * GB, BASE + 5 * GB], out_scale=BASE + 5 * GB + 12), sp.SP_ERR_SHAPE),
 ])
 def test_gather_rejects_invalid_problems(case, expect):
     status, msg = _gather(**case)
