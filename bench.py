@@ -551,7 +551,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused shard kernel runs on one rank's shard "
-              "and no collective is part of this build; run with --gpus 1", file=sys.stderr)
+              "and the library has no collective path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.quant == "fp8" and args.path != "gemm":
