@@ -18,8 +18,8 @@ import oracle
 import reduce_add_rmsnorm_amd as sp
 from helpers import bf16_bits_to_f64, e4m3_decode, to_host
 from parity import DEFAULT_WORKERS, run_case
-from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR,
-                                           WORKLOADS, make_inputs)
+from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK, QUANT_NONE,
+                                           QUANT_STATIC_TENSOR, WORKLOADS, make_inputs)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -111,6 +111,21 @@ def test_ragged_and_large_hidden(dev, H):
     w = variant("C2", hidden=H, num_tokens=8 * 6 - 3, num_tokens_pad=8 * 6)
     say(f"ragged H={H} tp=8 S=6 rank 7 (3 padding rows)")
     run_case(w, 7, dev=dev)
+
+
+@pytest.mark.parametrize("quant,fp4", [(QUANT_STATIC_TENSOR, False), (QUANT_DYNAMIC_TOKEN, False),
+                                       (QUANT_MX_BLOCK, False), (QUANT_MX_BLOCK, True)])
+@pytest.mark.parametrize("tp,H,pt", [(2, 16384, torch.bfloat16), (16, 16384, torch.bfloat16),
+                                     (4, 32768, torch.bfloat16), (3, 32768, torch.float32)])
+def test_quantised_outputs_at_large_hidden(dev, quant, fp4, tp, H, pt):
+    # every quantised output from the 4-vectors-per-thread kernels (tp = 2:
+    # every load in flight; tp = 16: partials in groups) and the 8-vector
+    # ones (groups), f32 partials, and a bias (per-token scaling then takes a
+    # second pass over the row)
+    w = variant("C3", tp=tp, hidden=H, partial_dtype=pt, quant_mode=quant, out_dtype=torch.uint8,
+                bias=True, num_tokens=tp * 6 - 3, num_tokens_pad=tp * 6)
+    say(f"quant={quant} fp4={fp4} tp={tp} H={H} partials={pt} S=6 rank {tp - 1} (3 padding rows)")
+    run_case(w, tp - 1, dev=dev, fp4=fp4, static_scale=0.01 if quant == QUANT_STATIC_TENSOR else None)
 
 
 @pytest.mark.parametrize("tp", [1, 3, 5, 16, 64])
