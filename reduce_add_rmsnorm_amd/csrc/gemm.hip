@@ -141,7 +141,10 @@ __global__ void __launch_bounds__(kThreads) matmul_scatter_kernel(const MArgs a)
   tile_of(a, &tm, &tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave-uniform in a scalar register, so that the LDS destinations of the
+  // direct-to-LDS loads (M0) are scalar arithmetic, not a VALU result read
+  // back per load
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // tokens [wm*64, +64), columns [wn*128, +128)
 
   // per-tile descriptors: rows past M (N) read as zero
