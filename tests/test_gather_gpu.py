@@ -12,11 +12,9 @@ import torch
 
 import oracle
 import reduce_add_rmsnorm_amd as sp
-from helpers import (bf16_bits_to_f64, bf16_round, e4m3_decode, e4m3_round, to_host,
-                     within_rounding, y_error, z_error)
+from helpers import bf16_bits_to_f64, bf16_round, to_host, within_rounding, y_error, z_error
 from parity import run_case
-from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_NONE, QUANT_STATIC_TENSOR,
-                                           WORKLOADS, make_inputs)
+from reduce_add_rmsnorm_amd.inputs import QUANT_DYNAMIC_TOKEN, QUANT_NONE, WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 

@@ -12,7 +12,7 @@ import torch
 import oracle
 import reduce_add_rmsnorm_amd as sp
 from helpers import to_host
-from parity import e2m1_decode, run_case, unpack_e2m1
+from parity import run_case, unpack_e2m1
 from reduce_add_rmsnorm_amd.inputs import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu

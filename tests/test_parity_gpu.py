@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import reduce_add_rmsnorm_amd as sp
-from helpers import bf16_bits_to_f64, e4m3_decode, to_host
+from helpers import e4m3_decode, to_host
 from parity import DEFAULT_WORKERS, run_case
 from reduce_add_rmsnorm_amd.inputs import (QUANT_DYNAMIC_TOKEN, QUANT_MX_BLOCK, QUANT_NONE,
                                            QUANT_STATIC_TENSOR, WORKLOADS, make_inputs)
