@@ -102,6 +102,63 @@ def test_layer_tail_graph_replays_match_eager(dev, fp8_producer):
     print(f"graph chain ok: {tp} producer + {tp} fused + 1 gather launches per replay", flush=True)
 
 
+def test_regroupings_graph_replays_match_eager(dev):
+    # FlashComm2's o_proj input regrouping (G = 4, otp = 2) and DSA-CP's
+    # head-to-token exchange (tp = 4), every rank, captured together
+    G, otp, N, C = 4, 2, 64, 96
+    tp, S, D = 4, 24, 40
+    print(f"graph regroupings: fc2 G={G} otp={otp} N={N} C={C}; dsacp tp={tp} S={S} D={D}", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    odp = G // otp
+    srcs = [torch.randn((N, C), generator=g, device=dev).to(torch.bfloat16) for _ in range(G)]
+    dsts = [torch.empty((N // odp, odp * C), dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    attn = [torch.randn((S, tp * D), generator=g, device=dev).to(torch.bfloat16) for _ in range(tp)]
+    outs = [torch.empty((tp * S, D), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
+    outputs = dsts + outs
+
+    def regroup():
+        sp.sp_fc2_regroup(srcs, dsts, otp=otp)
+        sp.sp_dsacp_heads_to_tokens(attn, outs)
+
+    regroup()
+    torch.cuda.synchronize()
+    ref = [_bits(t) for t in outputs]
+    # DSA-CP: rank q's output row p*S + s is head block q of rank p's token s
+    for q in range(tp):
+        want = torch.cat([attn[p][:, q * D:(q + 1) * D] for p in range(tp)])
+        assert torch.equal(outs[q], want)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        regroup()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        regroup()
+    for it in range(3):
+        for t in outputs:
+            t.view(torch.uint8).fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (a, t) in enumerate(zip(ref, outputs)):
+            assert torch.equal(a, _bits(t)), f"replay {it}: output {k} differs from the eager calls"
+    # inputs changed between replays are read at replay time
+    srcs[1].neg_()
+    attn[2].neg_()
+    graph.replay()
+    torch.cuda.synchronize()
+    replayed = [_bits(t) for t in outputs]
+    regroup()
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, _bits(t)) for a, t in zip(replayed, outputs))
+    assert any(not torch.equal(a, b) for a, b in zip(replayed, ref))
+    print("graph regroupings ok", flush=True)
+
+
 def test_calls_follow_the_given_stream(dev):
     """A call given a side stream through `stream` runs there, after the work
     enqueued on that stream just before it (here the product it reads)."""
