@@ -495,6 +495,54 @@ def also_fused(name, args, dev):
     return rec
 
 
+def hbm_ceilings(args, dev):
+    """HBM rates that plain streaming kernels of torch and the HIP runtime
+    reach on this part, to read the fused kernel's figures against: a
+    read-mostly reduction (a sum over the first dim of 64 planes: one byte
+    written per 64 read), a write-only fill and a device copy over MIB MiB
+    each (far past the 256 MB Infinity Cache), and torch's own sums of C4's
+    eight and C5's four partial planes (the fused kernel's reduce step alone,
+    tp read streams and one write stream).  HIP events around K launches
+    after W warm-up launches."""
+    n = args.ceilings << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src64 = src.view(64, -1)
+    red = torch.empty((src64.shape[1],), dtype=torch.float32, device=dev)
+    cases = {
+        "read: torch.sum over the first dim of 64 float32 planes": (
+            lambda: torch.sum(src64, dim=0, out=red), n, n // 64),
+        "write: fill_ of a float32 tensor": (lambda: dst.fill_(1.0), 0, n),
+        "copy: device-to-device copy_": (lambda: dst.copy_(src), n, n),
+    }
+    for name in ("C4", "C5"):
+        w = WORKLOADS[name]
+        planes = torch.ones((w.tp, w.shard_rows, w.hidden), dtype=torch.bfloat16, device=dev)
+        psum = torch.empty((w.shard_rows, w.hidden), dtype=torch.bfloat16, device=dev)
+        pb = planes.numel() * 2
+        cases[f"{name} partials: torch.sum over the {w.tp} bf16 planes"] = (
+            lambda planes=planes, psum=psum: torch.sum(planes, dim=0, out=psum), pb, pb // w.tp)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, (f, nr, nw) in cases.items():
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / args.steps
+        res[name] = {"bytes_read": nr, "bytes_written": nw, "us": round(us, 2),
+                     "gbs": round((nr + nw) / us / 1e3, 1),
+                     "frac_of_peak": round((nr + nw) / us / 1e3 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"hbm_ceilings": res, "mib": args.ceilings, "steps": args.steps,
+                      "warmup": args.warmup}), flush=True)
+
+
 def copy_calibration(args, dev):
     """A device-to-device copy of known size: every launch reads and writes
     exactly n bytes, which fixes the scale of FETCH_SIZE / WRITE_SIZE."""
@@ -546,6 +594,9 @@ def main():
                     help="fused path: further workloads timed with the same protocol before the "
                          "headline's inputs are allocated, reported under 'also' in the same line (default: C4 "
                          "when the headline is the default C5 run; '' for none)")
+    ap.add_argument("--ceilings", type=int, default=0, metavar="MIB",
+                    help="time plain streaming kernels (read-only sum, fill, copy over MIB MiB, and "
+                         "torch's sum of C4's partial planes) instead of the path, for reference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the path, time a plain device copy of MIB MiB (the "
                          "reference kernel for scaling hardware byte counters)")
@@ -566,6 +617,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(args, dev)
+        return
+    if args.ceilings:
+        hbm_ceilings(args, dev)
         return
     w = WORKLOADS[args.workload]
     fp8_gemm = args.path == "gemm" and args.quant == "fp8"
